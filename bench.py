@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused tensor-parallel BF16 GEMM + reduction on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the fused kernel over one batch of synthetic input
+already resident in HBM.  The default workload is the M=4096, N=6288, K=7168
+GEMM-AR with 7 emulated peer partials.  W untimed steps run first, then K
+steps are timed back to back with HIP events on the stream the kernel is
+launched on; one JSON line goes to stdout.
+
+Besides the throughput, the line carries
+  roofline      the kernel's algorithmic flops per launch over its measured
+                average launch time, against the MI355X dense bf16 MFMA peak,
+                and the HBM traffic per launch measured by rocprofv3 counters
+                (profiles/traffic.json; null when the kernel source changed
+                since the counters were taken)
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+                on this host's cores (a reported baseline, not the target)
+
+One GPU only: there is no multi-GPU path, and --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+METRIC = "TFLOP/s + % bf16 MFMA peak, fused GEMM-AR at M=4096,N=6288,K=7168"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "tensor_bf16_gemm_amd", "csrc", f)
+                  for f in ("gc_kernel.hpp", "gemm_coll.hip")]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Each operand once: A, B, the peer rows actually read, the outputs."""
+    e = 2
+    if w.mode == "ag":
+        return e * (w.R * w.M * w.K + w.K * w.N + w.R * w.M * w.N)
+    base = e * (w.M * w.K + w.K * w.N)
+    if w.mode == "ar":
+        return base + e * ((w.R - 1) * w.M * w.N + w.M * w.N)
+    P = -(-w.M // w.R)
+    lo, hi = min(w.rank * P, w.M), min(w.rank * P + P, w.M)
+    owned = hi - lo
+    return base + e * ((w.R - 1) * owned * w.N + P * w.N + (w.M - owned) * w.N)
+
+
+def make_step(w, x):
+    import torch
+    import tensor_bf16_gemm_amd as gc
+    dev = x["B"].device
+    if w.mode == "ar":
+        out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        return lambda: gc.gemm_ar(x["A"], x["B"], x["peers"], out, R=w.R, rank=w.rank)
+    if w.mode == "rs":
+        P = -(-w.M // w.R)
+        out = torch.empty((P, w.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        return lambda: gc.gemm_rs(x["A"], x["B"], x["peers"], ws, out, R=w.R, rank=w.rank)
+    out = torch.empty((w.R * w.M, w.N), dtype=torch.bfloat16, device=dev)
+    flags = torch.ones(w.R, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    return lambda: gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, out, R=w.R,
+                              rank=w.rank, epoch=1)
+
+
+def read_traffic(w, kernel_us: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source for this workload."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("workloads", {}).get(w.name)
+    if not entry or entry.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, target_s: float):
+    """Time the CPU oracle on leading rows of the workload (about target_s)."""
+    import torch
+    from oracle.oracle import load
+    from workloads import bits
+    orc = load()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    B = bits(x["B"].cpu())
+    if w.mode == "ag":
+        src = x["A"]
+        peer_fn = lambda rows: None
+        total_rows = w.R * w.M
+    else:
+        src = x["A"]
+        peer_fn = lambda rows: bits(x["peers"][:, :rows].cpu().contiguous())
+        total_rows = w.M
+
+    def run(rows):
+        A = bits(src[:rows].cpu().contiguous())
+        P = peer_fn(rows)
+        t0 = time.perf_counter()
+        orc.ar_rows(A, B, P)
+        return time.perf_counter() - t0
+
+    probe = min(16, src.shape[0])
+    dt = run(probe)
+    rows = max(probe, min(src.shape[0], int(probe * target_s / max(dt, 1e-6))))
+    dt = run(rows)
+    flops = 2.0 * rows * w.N * w.K
+    peers = "" if w.mode == "ag" else f", {w.R - 1} peer partials"
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of {total_rows} ({w.name}: all {w.N} columns, "
+                  f"K={w.K}{peers}); {dt:.1f} s; fp64 accumulation, plain loops",
+        "seconds": dt,
+        "rows": rows,
+        "cpu": cpu_model(),
+    }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the peer ranks are emulated by buffers in this GPU's memory); "
+              "run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import tensor_bf16_gemm_amd as gc
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    gc.lib()  # fail loudly if the library is missing
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return 0
+
+    name = args.workload or wl.HEADLINE
+    w = wl.WORKLOADS[name]
+    x = wl.make_inputs(w, device="cuda")
+    step = make_step(w, x)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / max(args.steps, 1)
+
+    flops = w.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    abytes = algorithmic_bytes(w)
+    traffic = read_traffic(w, ms * 1e3)
+    line = {
+        "metric": METRIC if name == wl.HEADLINE else f"TFLOP/s, fused {w.mode.upper()} {name}",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "mode": w.mode, "M": w.M, "N": w.N, "K": w.K, "R": w.R,
+                   "rank": w.rank, "global_batch": w.M * (w.R if w.mode == "ag" else 1),
+                   "parallelism": f"tp{w.R} emulated on 1 GPU"},
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "algorithmic_bytes": abytes,
+            "hbm_frac_of_step": (abytes / (ms * 1e-3)) / (PEAK_HBM_GBS * 1e9),
+            "kernel": f"gc_kernel mode {w.mode}",
+            "timing": "HIP events on the launch stream around the timed steps",
+        },
+        "wall_s": wall,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

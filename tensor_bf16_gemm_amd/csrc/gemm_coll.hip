@@ -1,0 +1,211 @@
+// gemm_coll.hip -- host side of the C ABI declared in include/gemm_coll.h:
+// argument validation, tile-configuration choice and the launch on the
+// caller's stream.  Device code lives in gc_kernel.hpp.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <atomic>
+
+#include "gc_kernel.hpp"
+#include "gemm_coll.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+int cu_count(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Every buffer is addressed through 32-bit byte offsets with an out-of-range
+// sentinel at 2^31, so each one must stay below 2 GiB.
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
+
+bool fits(int64_t rows, int64_t cols) { return rows * cols * 2 < kMaxBufferBytes; }
+
+int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R,
+                 int rank, const gc_peers *peers, const gc_bf16 *out)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return GC_EINVAL;
+    if (!(R > 1 && R <= 16 && 128 % R == 0))
+        return GC_EINVAL;
+    if (rank < 0 || rank >= R)
+        return GC_EINVAL;
+    if (N % 8 != 0 || K % 8 != 0)
+        return GC_EINVAL;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return GC_ENOTSUP;
+    if (M == 0 || N == 0)
+        return GC_OK;  // nothing to do; pointers may be NULL
+    if (!peers || !out || !aligned16(out))
+        return GC_EINVAL;
+    // A and B are not read when K == 0 (the output is then the peer sum).
+    if (K > 0 && (!A || !B || !aligned16(A) || !aligned16(B)))
+        return GC_EINVAL;
+    return GC_OK;
+}
+
+template <int BM, int BN, int MODE>
+int launch(gc::Args &a, hipStream_t stream, int dev)
+{
+    a.tiles_m = (a.m_rows + BM - 1) / BM;
+    a.tiles_n = (a.N + BN - 1) / BN;
+    const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
+    const int64_t total = MODE == gc::MODE_AG ? per * a.R : per;
+    if (total > INT32_MAX)
+        return GC_ENOTSUP;
+    a.num_tiles = (int)total;
+    a.group_m = 4;
+    if (a.num_tiles == 0)
+        return GC_OK;
+    const int grid = a.num_tiles < cu_count(dev) ? a.num_tiles : cu_count(dev);
+    hipLaunchKernelGGL((gc::gc_kernel<BM, BN, MODE>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
+}
+
+template <int MODE>
+int dispatch(gc::Args &a, hipStream_t stream)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GC_EIO;
+    return launch<256, 256, MODE>(a, stream, dev);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_coll_should_run(int64_t M) { return M >= 128 ? 1 : 0; }
+
+const char *gemm_coll_strerror(int code)
+{
+    switch (code) {
+    case GC_OK:
+        return "success";
+    case GC_EINVAL:
+        return "invalid argument (NULL or misaligned pointer, R or rank out of range, negative "
+               "size, or N/K not a multiple of 8)";
+    case GC_ENOTSUP:
+        return "shape not supported by this kernel set (a buffer of 2 GiB or more)";
+    case GC_EIO:
+        return "HIP kernel launch failed";
+    default:
+        if (code >= GC_TIMEOUT_BASE && code < GC_TIMEOUT_BASE + 16)
+            return "AG-GEMM: a shard's ready flag did not arrive in time";
+        return "unknown error code";
+    }
+}
+
+int gemm_ar(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
+            const gc_peers *peers, gc_bf16 *out, void *stream)
+{
+    int err = check_common(A, B, M, N, K, R, rank, peers, out);
+    if (err || M == 0 || N == 0)
+        return err;
+    if (!peers->partials || !aligned16(peers->partials))
+        return GC_EINVAL;
+    if (!fits(M, K) || !fits(K, N) || !fits(M, N))
+        return GC_ENOTSUP;
+    gc::Args a = {};
+    a.A = A;
+    a.B = B;
+    a.partials = peers->partials;
+    a.out = out;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.R = R;
+    a.rank = rank;
+    a.npeers = R - 1;
+    a.m_rows = (int)M;
+    return dispatch<gc::MODE_AR>(a, (hipStream_t)stream);
+}
+
+int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
+            const gc_peers *peers, gc_bf16 *out, void *stream)
+{
+    int err = check_common(A, B, M, N, K, R, rank, peers, out);
+    if (err || M == 0 || N == 0)
+        return err;
+    if (!peers->partials || !aligned16(peers->partials) || !peers->ws || !aligned16(peers->ws))
+        return GC_EINVAL;
+    if (!fits(M, K) || !fits(K, N) || !fits(M, N))
+        return GC_ENOTSUP;
+    if (M == 0 || N == 0)
+        return GC_OK;
+    // Slice of rank r: P = ceil(M/R) rows, global rows [r*P, (r+1)*P);
+    // the valid ones are those below M.
+    const int64_t P = (M + R - 1) / R;
+    int64_t lo = (int64_t)rank * P, hi = lo + P;
+    const int64_t end = hi;  // last slice row + 1 (may exceed M: padding)
+    if (lo > M)
+        lo = M;
+    if (hi > M)
+        hi = M;
+    gc::Args a = {};
+    a.A = A;
+    a.B = B;
+    a.partials = peers->partials;
+    a.out = out;
+    a.ws = peers->ws;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.R = R;
+    a.rank = rank;
+    a.npeers = R - 1;
+    a.P = (int)P;
+    a.lo = (int)lo;
+    a.hi = (int)hi;
+    a.m_rows = (int)(end > M ? end : M);
+    return dispatch<gc::MODE_RS>(a, (hipStream_t)stream);
+}
+
+int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K, int R, int rank,
+            const gc_peers *peers, gc_bf16 *out, void *stream)
+{
+    int err = check_common(A, B, Ms, N, K, R, rank, peers, out);
+    if (err || Ms == 0 || N == 0)
+        return err;
+    if (!peers->shards || !aligned16(peers->shards) || !peers->flags ||
+        ((uintptr_t)peers->flags & 3u) || !peers->status || ((uintptr_t)peers->status & 3u))
+        return GC_EINVAL;
+    if (!fits(Ms, K) || !fits(K, N) || !fits(Ms * R, N))
+        return GC_ENOTSUP;
+    gc::Args a = {};
+    a.A = A;
+    a.B = B;
+    a.shards = peers->shards;
+    a.flags = peers->flags;
+    a.status = peers->status;
+    a.epoch = peers->epoch;
+    // A poll is one system-scope load (about a microsecond) plus a short
+    // s_sleep; the default bound gives up after one to two seconds.
+    a.max_spins = peers->max_spins ? peers->max_spins : (1u << 20);
+    a.out = out;
+    a.M = (int)Ms;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.R = R;
+    a.rank = rank;
+    a.m_rows = (int)Ms;
+    return dispatch<gc::MODE_AG>(a, (hipStream_t)stream);
+}
+
+}  // extern "C"
