@@ -2,30 +2,47 @@
 //
 // One persistent kernel template serves the three modes:
 //   AR  out = bf16(acc + sum of the R-1 peer partials)          (all rows)
-//   RS  owned rows as AR into out; other valid rows bf16(acc) into ws
+//   RS  slice rows as AR into out; other valid rows bf16(acc) into ws
 //   AG  out rows of shard q = bf16(acc); shards taken in ring order, each
 //       behind a ready flag polled in the kernel
-// (GEMM-AR / GEMM-RS: "[Kimi-K3] Extend GEMM-RS to GEMM-AR", 实现拆解 step 1;
-//  AG-GEMM: "[Kimi-K3] AG-GEMM for Sequence Parallelism", Purpose, and the
-//  closing remark under its component breakdown table about one GEMM kernel
-//  that waits inside the kernel.)
+// (GEMM-AR / GEMM-RS: "[Kimi-K3] Extend GEMM-RS to GEMM-AR", 实现拆解 step 1
+//  and the test reference in 关键源码片段; AG-GEMM: "[Kimi-K3] AG-GEMM for
+//  Sequence Parallelism", Purpose, Implementation details, and the remark
+//  under its component breakdown table about one GEMM kernel that waits
+//  inside the kernel.)
 //
-// Mainloop (CDNA4): a BM x BN block tile, BK = 64, four waves in a 2 x 2
-// grid, each wave owning a (BM/2) x (BN/2) sub-tile of 16 x 16 fp32
-// accumulator blocks fed by v_mfma_f32_16x16x32_bf16.  Both operands are
-// staged in LDS, double-buffered, as K-contiguous rows of 64 bf16 (128 B):
-//   A tile   [BM rows of m][64 k]  loaded from A[M][K] as-is
-//   B^T tile [BN rows of n][64 k]  B[K][N] is N-contiguous, so each thread
-//            loads an 8(k) x 8(n) block with 16-byte loads and transposes it
-//            in registers (v_perm_b32) before the LDS store
-// The 16-byte chunks of a row are XOR-swizzled with (row/2)%8 so that the
-// 16 lanes of every ds_read_b128 / ds_write_b128 phase hit 16 distinct
-// 4-bank groups of the 64-bank LDS.
+// Tile: 256 x 256 outputs per workgroup, K in steps of 64, four waves in a
+// 2 x 2 grid, each wave owning 128 x 128 outputs as 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16.
 //
-// The MFMA is issued with B^T as its first operand and A as its second, so
-// the 16 x 16 result block it produces is C^T: lane l holds C[m = l%16]
-// [n = 4*(l/16) .. 4*(l/16)+3], four consecutive columns of one output row.
-// The epilogue therefore reads peers and writes outputs as 8-byte vectors.
+// Operand staging (two LDS stages of 64 KiB):
+//   A tile  [256 m][64 k]  128 B per row; 16-byte chunk c of row m is stored
+//           at chunk c ^ ((m/2) % 8), so the 16 lanes of a ds_read_b128
+//           phase cover all 64 banks.
+//   B tile  [64 k][256 n]  512 B per row (B is N-contiguous and stays so);
+//           32-byte chunk q of row k is stored at q ^ f(k) with
+//           f(k) = (k % 4) + 4 * ((k / 8) % 2), so the 32 lanes of a
+//           ds_read_b64_tr_b16 pass cover all 64 banks.
+// Both tiles move global -> LDS with 16-byte buffer loads that write LDS
+// directly (no VGPR staging); each wave instruction fills 1 KiB of LDS in
+// lane order, so the swizzle is applied by choosing which global chunk each
+// lane fetches.  Loads past M, N or K return zeros (buffer range check).
+//
+// Fragments: the MFMA's first operand is B^T (n rows, 8 consecutive k per
+// lane), read with two ds_read_b64_tr_b16 per block: within each 16-lane
+// group, lane j receives element j%4 of the 8-byte chunks addressed by
+// lanes 4e + j/4 (e = 0..3), so lanes that address rows k..k+3 at column
+// offsets 0,4,8,12 deliver to lane j the four k-values of column j.  The
+// second operand is A (m rows) read with ds_read_b128.  The 16 x 16 result
+// block is then C^T in MFMA layout: lane l holds row m = l%16, columns
+// n = 4*(l/16) .. +3 -- four consecutive outputs, 8 bytes in memory.
+//
+// Peer partials (AR, RS): the R-1 peer tiles are added into the fp32
+// accumulators while the K loop runs.  Item w = (peer w/8, row block w%8)
+// is loaded (8 x 8-byte buffer loads per lane) at K-step w-2 and added at
+// K-step w, so the peer traffic streams behind the MFMA work instead of
+// forming an epilogue; items beyond the K loop are added after it, eight
+// items per round trip.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,8 +53,9 @@ namespace gc {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 enum Mode { MODE_AR = 0, MODE_RS = 1, MODE_AG = 2 };
 
@@ -64,8 +82,15 @@ struct Args {
     int group_m;               // row tiles per L2 group
 };
 
-// Out-of-range offset for buffer loads: every buffer we address is < 2 GiB,
-// so this offset is always past num_records and the load returns zeros.
+constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+constexpr int WAVES = NT / 64;             // 8: 2 (m) x 4 (n)
+constexpr int WM = 128, WN = 64, FM = 8, FN = 4;
+constexpr int A_BYTES = BM * BK * 2;       // 32 KiB
+constexpr int B_BYTES = BK * BN * 2;       // 32 KiB
+constexpr int PSLOT = 16 * WN * 2;         // one peer block of a wave: 2 KiB
+
+// Out-of-range offset for buffer accesses: every buffer addressed here is
+// < 2 GiB, so this offset is past num_records; loads return 0, stores drop.
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUFFER_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
 
@@ -75,9 +100,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
                                              BUFFER_FLAGS);
 }
 
-__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// 16 bytes global -> LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void_t *lds_base, uint32_t off)
 {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (int)off, 0, 0, 0);
+}
+
+// 8-byte buffer load / store; `soff` is a wave-uniform byte offset added by
+// the hardware (an SGPR), so one VGPR offset serves several columns.
+__device__ __forceinline__ u32x2_t load8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0);
+}
+
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v,
+                                       uint32_t soff = 0)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, (int)soff, 0);
 }
 
 // fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
@@ -98,6 +137,23 @@ __device__ __forceinline__ f32x4_t unpack_bf16x4(u32x2_t w)
     return r;
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the compiler's implicit "vmcnt(0)" that a
+// __syncthreads() gets while LDS-DMA loads are pending: every caller waits
+// explicitly for exactly the loads the barrier must cover.
+__device__ __forceinline__ void barrier_only()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Logical tile of workgroup `b` in one round of `G` workgroups.  Workgroups
 // are dispatched round-robin over the 8 XCDs (b % 8); each XCD is handed a
 // contiguous run of logical tiles so that the tiles resident on one XCD share
@@ -109,60 +165,54 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
     return x * base + (x < rem ? x : rem) + j;
 }
 
-template <int BM, int BN>
-struct Tile {
-    static constexpr int BK = 64;
-    static constexpr int NT = 256;            // threads
-    static constexpr int WM = BM / 2;         // wave sub-tile rows (m)
-    static constexpr int WN = BN / 2;         // wave sub-tile cols (n)
-    static constexpr int FM = WM / 16;        // 16x16 blocks per wave along m
-    static constexpr int FN = WN / 16;        // ... along n
-    static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BN * BK * 2;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int A_ITERS = BM * BK / 8 / NT;          // 16-byte chunks per thread
-    static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);      // 8x8 blocks per tile
-    static constexpr int B_ITERS = B_BLOCKS >= NT ? B_BLOCKS / NT : 1;
-    static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
-    static_assert(BM * BK / 8 % NT == 0, "A loader");
-    static_assert(B_BLOCKS % NT == 0 || NT % B_BLOCKS == 0, "B loader");
-};
-
-// Byte offset of 16-byte chunk `c` (0..7) of LDS row `row` (128 B per row).
-__device__ __forceinline__ uint32_t lds_off(int row, int c)
+template <int MODE>
+__global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
-    return (uint32_t)(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-}
-
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256, 1) void gc_kernel(Args p)
-{
-    using T = Tile<BM, BN>;
-    constexpr int BK = T::BK;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
+    // One array per operand and stage: distinct LDS objects carry distinct
+    // alias scopes, so the compiler knows the loads filling stage s+1 cannot
+    // alias the fragment reads of stage s and does not wait for them.
+    __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sA1[A_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sB1[B_BYTES];
+    // Peer staging (AR / RS): two slots of one 16 x 64 bf16 block per wave.
+    __shared__ __attribute__((aligned(16))) uint8_t sP0[WAVES * PSLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t sP1[WAVES * PSLOT];
     __shared__ int s_ready;
+    constexpr bool PEERS = MODE != MODE_AG;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
     const int G = gridDim.x;
-
-    const uint32_t b_bytes = (uint32_t)p.K * (uint32_t)p.N * 2u;
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B, b_bytes);
     const int KT = (p.K + BK - 1) / BK;
+    const uint32_t N2 = (uint32_t)p.N * 2u;
 
-    // Loader coordinates (fixed per thread).
-    const int a_kc = tid & 7;        // A: 16-byte chunk within the 64-k row
-    const int a_r0 = tid >> 3;       // A: first row (rows a_r0 + 32*i)
-    const int b_kc = tid & 7;        // B: k-chunk of the 8x8 block
-    const int b_nc = tid >> 3;       // B: n-chunk of the 8x8 block (+32*i)
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B, (uint32_t)p.K * N2);
 
-    // MFMA fragment read offsets: lane row l%16, k-chunk ks*4 + l/16.
-    const int fr = lane & 15;
-    const uint32_t frag_off0 = lds_off(fr, 0 + (lane >> 4));
-    const uint32_t frag_off1 = lds_off(fr, 4 + (lane >> 4));
+    // ---- per-lane constants -------------------------------------------------
+    // A loader: wave instruction j (0..3) fills LDS rows 32*wave + 8*j + lane/8
+    // (128 B each); the lane's stored chunk lane%8 holds logical chunk
+    // (lane%8) ^ ((row/2)%8) = (lane%8) ^ ((4*j + lane/16) % 8).
+    const int a_c_even = (lane & 7) ^ ((lane >> 4) & 7);          // j even
+    const int a_c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);     // j odd
+    // B loader: wave instruction j (0..3) fills LDS rows k = 8*wave + 2*j +
+    // lane/32 (512 B each); the lane's stored 16-byte slot lane%32 is half
+    // lane%2 of stored 32-byte chunk (lane%32)/2 = logical chunk ^ f(k), with
+    // f(k) = (k%4) + 4*((k/8)%2) = ((2*j + lane/32) % 4) + 4*(wave%2).
+    const int b_slot = lane & 31;
+    // fragment reads
+    const int fi = lane & 15, fg = lane >> 4;
+    const uint32_t a_frag0 = (uint32_t)(wm * WM * 128 + fi * 128 + ((0 + fg) ^ (fi >> 1)) * 16);
+    const uint32_t a_frag1 = (uint32_t)(wm * WM * 128 + fi * 128 + ((4 + fg) ^ (fi >> 1)) * 16);
+    const int fB = (fi >> 2) | ((fg & 1) << 2);
+    // B^T block j of this wave is logical 32-byte chunk q = 4*wn + j.
+    const uint32_t b_frag = (uint32_t)((8 * fg + (fi >> 2)) * 512 + (wn >> 1) * 256 + 8 * (fi & 3));
+    uint32_t b_frag_j[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        b_frag_j[j] = b_frag + (uint32_t)(((4 * (wn & 1) + j) ^ fB) * 32);
 
     for (int round = 0;; ++round) {
         const int lin = round * G;
@@ -173,8 +223,8 @@ __global__ __launch_bounds__(256, 1) void gc_kernel(Args p)
             break;
         const int L = lin + xcd_remap(blockIdx.x, live);
 
-        // Decode the tile: shard step s (AG), row tile mt, column tile nt,
-        // grouped column-major over `group_m` row tiles for L2 reuse.
+        // Tile: shard step s (AG), row tile mt, column tile nt, grouped
+        // column-major over `group_m` row tiles for L2 reuse.
         int s = 0, t = L;
         const int per_shard = p.tiles_m * p.tiles_n;
         if (MODE == MODE_AG) {
@@ -189,6 +239,8 @@ __global__ __launch_bounds__(256, 1) void gc_kernel(Args p)
         const int mt = gm0 + in_g % gh;
         const int nt = in_g / gh;
         const int m0 = mt * BM, n0 = nt * BN;
+
+        __syncthreads();  // LDS of the previous tile is no longer read
 
         const uint16_t *Asrc = p.A;
         int q = 0;
@@ -223,160 +275,233 @@ __global__ __launch_bounds__(256, 1) void gc_kernel(Args p)
                     continue;
             }
         }
-        const uint32_t a_bytes = (uint32_t)p.M * (uint32_t)p.K * 2u;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(Asrc, a_bytes);
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(Asrc, (uint32_t)p.M * (uint32_t)p.K * 2u);
 
-        // Per-thread global row validity.
-        bool a_ok[T::A_ITERS];
+        // ---- loader offsets for this tile at k0 = 0 (rows past M and
+        // columns past N already folded into OOB); a step adds its k0 ----
+        uint32_t a_off[4], b_off[4];
+        int a_kc[4], b_k[4];
 #pragma unroll
-        for (int i = 0; i < T::A_ITERS; ++i)
-            a_ok[i] = (m0 + a_r0 + 32 * i) < p.M;
-        bool b_ok[T::B_ITERS];
-        bool b_active[T::B_ITERS];
-#pragma unroll
-        for (int i = 0; i < T::B_ITERS; ++i) {
-            b_active[i] = (tid + T::NT * i) < T::B_BLOCKS;
-            b_ok[i] = b_active[i] && (n0 + (b_nc + 32 * i) * 8) < p.N;
+        for (int j = 0; j < 4; ++j) {
+            const int row = m0 + 32 * wave + 8 * j + (lane >> 3);
+            const int c = (j & 1) ? a_c_odd : a_c_even;
+            a_kc[j] = 8 * c;
+            a_off[j] = row < p.M ? ((uint32_t)row * (uint32_t)p.K + (uint32_t)(8 * c)) * 2u : OOB;
+            const int k = 8 * wave + 2 * j + (lane >> 5);
+            const int fk = (k & 3) | (((k >> 3) & 1) << 2);
+            const int n = n0 + 16 * ((b_slot >> 1) ^ fk) + 8 * (b_slot & 1);
+            b_k[j] = k;
+            b_off[j] = n < p.N ? ((uint32_t)k * (uint32_t)p.N + (uint32_t)n) * 2u : OOB;
         }
-
-        u32x4_t ga[T::A_ITERS];
-        u32x4_t gb[T::B_ITERS][8];
-
-        auto gload = [&](int k0) {
-            const int ka = k0 + a_kc * 8;
+        auto dma_stage = [&](int kt, uint8_t *sa, uint8_t *sb) {
+            const int k0 = kt * BK;
+            const uint32_t ka = (uint32_t)k0 * 2u, kb = (uint32_t)k0 * N2;
+            if (k0 + BK <= p.K) {   // whole step inside K: no per-lane K test
 #pragma unroll
-            for (int i = 0; i < T::A_ITERS; ++i) {
-                const uint32_t off = (a_ok[i] && ka < p.K)
-                    ? ((uint32_t)(m0 + a_r0 + 32 * i) * (uint32_t)p.K + (uint32_t)ka) * 2u
-                    : OOB;
-                ga[i] = bload16(rA, off);
-            }
+                for (int j = 0; j < 4; ++j)
+                    dma16(rA, (lds_void_t *)(sa + (32 * wave + 8 * j) * 128), a_off[j] + ka);
 #pragma unroll
-            for (int i = 0; i < T::B_ITERS; ++i) {
-                const uint32_t ncol = (uint32_t)(n0 + (b_nc + 32 * i) * 8);
+                for (int j = 0; j < 4; ++j)
+                    dma16(rB, (lds_void_t *)(sb + (8 * wave + 2 * j) * 512), b_off[j] + kb);
+            } else {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int kr = k0 + b_kc * 8 + r;
-                    const uint32_t off = (b_ok[i] && kr < p.K)
-                        ? ((uint32_t)kr * (uint32_t)p.N + ncol) * 2u
-                        : OOB;
-                    gb[i][r] = bload16(rB, off);
-                }
+                for (int j = 0; j < 4; ++j)
+                    dma16(rA, (lds_void_t *)(sa + (32 * wave + 8 * j) * 128),
+                          k0 + a_kc[j] < p.K ? a_off[j] + ka : OOB);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dma16(rB, (lds_void_t *)(sb + (8 * wave + 2 * j) * 512),
+                          k0 + b_k[j] < p.K ? b_off[j] + kb : OOB);
             }
         };
 
-        auto lstore = [&](int stage) {
-            uint8_t *sA = smem + stage * T::STAGE;
-            uint8_t *sB = sA + T::A_BYTES;
+        // ---- peer items (AR / RS) ----
+        // Rows of this wave's blocks: m = m0 + wm*128 + 16*i + lane%16;
+        // columns n = n0 + wn*64 + 16*j + 4*(lane/16).  Peer rows outside
+        // [row_lo, row_hi) read as zero through the buffer range check.
+        const int pm_base = m0 + wm * WM + fi;
+        const int pn_base = n0 + wn * WN + 4 * fg;
+        const int row_lo = MODE == MODE_RS ? p.lo : 0;
+        const int row_hi = MODE == MODE_RS ? p.hi : p.M;
+        int W = 0;
+        if (PEERS && m0 < row_hi && m0 + BM > row_lo)
+            W = p.npeers * FM;
+        // Item (peer pp, row block i) is the wave's 16 x 64 block of that
+        // peer partial: rows blk .. blk+15 (blk = m0 + 128*wm + 16*i), columns
+        // n0 + 64*wn .. +63.  It moves global -> LDS with two 16-byte DMA
+        // instructions per wave (8 rows of 128 B each); 16-byte chunk c of
+        // block row r is stored at chunk c ^ ((r/2) % 8).  The buffer starts
+        // at the first row that may be read (>= row_lo) and ends at row_hi,
+        // so rows outside [row_lo, row_hi) read as zero (rows below wrap past
+        // 2^31); chunks past N are masked per lane on edge tiles.
+        uint32_t pd_off[2];
+        bool pd_ok[2];
 #pragma unroll
-            for (int i = 0; i < T::A_ITERS; ++i)
-                *(u32x4_t *)(sA + lds_off(a_r0 + 32 * i, a_kc)) = ga[i];
+        for (int r = 0; r < 2; ++r) {
+            const int row = 8 * r + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            const int n = n0 + wn * WN + 8 * c;
+            pd_off[r] = (uint32_t)row * N2 + (uint32_t)n * 2u;
+            pd_ok[r] = n < p.N;
+        }
+        auto peer_dma = [&](uint8_t *slotbuf, int pp, int i) {
+            const int blk = m0 + wm * WM + 16 * i;
+            const int start = max(blk, row_lo);
+            const int rows = max(row_hi - start, 0);
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(
+                p.partials + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
+            const uint32_t shift = (uint32_t)(start - blk) * N2;
 #pragma unroll
-            for (int i = 0; i < T::B_ITERS; ++i) {
-                if (!b_active[i])
-                    continue;
-                // Transpose the 8(k) x 8(n) block: w[j] = the 8 k-values of column j.
-                const u32x4_t *v = gb[i];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    u32x4_t lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lo[e] = __builtin_amdgcn_perm(v[2 * e + 1][d], v[2 * e][d], 0x05040100u);
-                        hi[e] = __builtin_amdgcn_perm(v[2 * e + 1][d], v[2 * e][d], 0x07060302u);
-                    }
-                    const int row = (b_nc + 32 * i) * 8 + 2 * d;
-                    *(u32x4_t *)(sB + lds_off(row, b_kc)) = lo;
-                    *(u32x4_t *)(sB + lds_off(row + 1, b_kc)) = hi;
-                }
-            }
+            for (int r = 0; r < 2; ++r)
+                dma16(rp, (lds_void_t *)(slotbuf + wave * PSLOT + r * 1024),
+                      pd_ok[r] ? pd_off[r] - shift : OOB);
         };
+        // Reading back: lane (fi, fg) needs row fi, columns 16*j + 4*fg .. +3,
+        // i.e. half fg%2 of logical chunk 2*j + fg/2.
+        uint32_t pc_off[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            pc_off[j] = (uint32_t)(fi * 128 + (((2 * j + (fg >> 1)) ^ ((fi >> 1) & 7)) << 4) +
+                                   8 * (fg & 1));
 
-        f32x4_t acc[T::FM][T::FN];
+        f32x4_t acc[FM][FN];
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j)
+            for (int j = 0; j < FN; ++j)
                 acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-        if (KT > 0) {
-            gload(0);
-            lstore(0);
-            __syncthreads();
-        }
-        for (int kt = 0; kt < KT; ++kt) {
-            const bool more = kt + 1 < KT;
-            if (more)
-                gload((kt + 1) * BK);
-            const uint8_t *sA = smem + (kt & 1) * T::STAGE;
-            const uint8_t *sB = sA + T::A_BYTES;
+        auto half_step = [&](const uint8_t *cA, const uint8_t *cB, int ks) {
+            bf16x8_t fa[FN], fb[FM];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint32_t fo = ks ? frag_off1 : frag_off0;
-                bf16x8_t fa[T::FN], fb[T::FM];
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-                    fa[j] = *(const bf16x8_t *)(sB + (wn * T::WN + j * 16) * 128 + fo);
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-                    fb[i] = *(const bf16x8_t *)(sA + (wm * T::WM + i * 16) * 128 + fo);
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < T::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j],
-                                                                            0, 0, 0);
+            for (int j = 0; j < FN; ++j) {
+                const uint8_t *base = cB + b_frag_j[j] + ks * 32 * 512;
+                bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
+                bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * 512));
+                fa[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            if (more)
-                lstore((kt + 1) & 1);
-            __syncthreads();
-        }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fb[i] = *(const bf16x8_t *)(cA + (ks ? a_frag1 : a_frag0) + i * 16 * 128);
+            // All twelve fragments are requested before the first MFMA, so
+            // their LDS latency overlaps instead of being paid per fragment.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
+        };
 
-        // ---------------- epilogue ----------------
-        const int mrow0 = m0 + wm * T::WM + (lane & 15);
-        const int ncol0 = n0 + wn * T::WN + 4 * (lane >> 4);
+        // prologue: item 0, stage 0, item 1  (the order the steps rely on)
+        if (PEERS && W > 0)
+            peer_dma(sP0, 0, 0);
+        if (KT > 0)
+            dma_stage(0, sA0, sB0);
+        if (PEERS && W > 1)
+            peer_dma(sP1, 0, 1);
+
+        // ---- main loop, unrolled by 8 so that the stage, the peer slot and
+        // the peer row block are compile-time constants.  Step kt: wait for
+        // the own loads of stage kt (only peer item kt+1 may still fly);
+        // barrier (everyone's stage kt landed, everyone done reading stage
+        // kt-1); loads of stage kt+1; add peer item kt and load item kt+2;
+        // MFMAs of stage kt. ----
+        for (int kt0 = 0; kt0 < KT; kt0 += 8) {
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-            const int m = mrow0 + i * 16;
+            for (int u = 0; u < 8; ++u) {
+                const int kt = kt0 + u;
+                if (kt < KT) {
+                    uint8_t *cA = (u & 1) ? sA1 : sA0;
+                    uint8_t *cB = (u & 1) ? sB1 : sB0;
+                    uint8_t *nA = (u & 1) ? sA0 : sA1;
+                    uint8_t *nB = (u & 1) ? sB0 : sB1;
+                    uint8_t *sl = (u & 1) ? sP1 : sP0;
+                    if (PEERS && kt + 1 < W)
+                        wait_vmcnt<2>();
+                    else
+                        wait_vmcnt<0>();
+                    barrier_only();
+                    if (kt + 1 < KT)
+                        dma_stage(kt + 1, nA, nB);
+                    if (PEERS) {
+                        if (kt < W) {
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-                const int n = ncol0 + j * 16;
-                if (n >= p.N)
-                    continue;
-                f32x4_t v = acc[i][j];
-                if (MODE == MODE_AR) {
-                    if (m >= p.M)
-                        continue;
-                    const size_t e = (size_t)m * p.N + n;
-                    const size_t slot = (size_t)p.M * p.N;
-                    for (int pp = 0; pp < p.npeers; ++pp)
-                        v += unpack_bf16x4(*(const u32x2_t *)(p.partials + pp * slot + e));
-                    *(u32x2_t *)(p.out + e) = pack_bf16x4(v);
-                } else if (MODE == MODE_RS) {
-                    if (m >= p.lo && m < p.hi) {
-                        const size_t e = (size_t)m * p.N + n;
-                        const size_t slot = (size_t)p.M * p.N;
-                        for (int pp = 0; pp < p.npeers; ++pp)
-                            v += unpack_bf16x4(*(const u32x2_t *)(p.partials + pp * slot + e));
-                        *(u32x2_t *)(p.out + (size_t)(m - p.lo) * p.N + n) = pack_bf16x4(v);
-                    } else if (m < p.M) {
-                        *(u32x2_t *)(p.ws + (size_t)m * p.N + n) = pack_bf16x4(v);
-                    } else {
-                        // padding rows of the slice: global rows [max(M, r*P), (r+1)*P)
-                        const int t_out = m - p.rank * p.P;
-                        if (t_out >= 0 && t_out < p.P)
-                            *(u32x2_t *)(p.out + (size_t)t_out * p.N + n) = (u32x2_t){0u, 0u};
+                            for (int j = 0; j < FN; ++j)
+                                acc[u][j] += unpack_bf16x4(
+                                    *(const u32x2_t *)(sl + wave * PSLOT + pc_off[j]));
+                        }
+                        if (kt + 2 < W)
+                            peer_dma(sl, (kt + 2) >> 3, (u + 2) & 7);
                     }
-                } else {  // AG
-                    if (m >= p.M)
-                        continue;
-                    *(u32x2_t *)(p.out + ((size_t)q * p.M + m) * p.N + n) = pack_bf16x4(v);
+                    half_step(cA, cB, 0);
+                    half_step(cA, cB, 1);
                 }
             }
         }
-        // No barrier needed here: every wave passed the mainloop's last
-        // barrier, so no LDS read is pending when the next tile's prologue
-        // writes stage 0.
+
+        // ---- peer items the K loop did not reach: two in flight ----
+        if (PEERS && W > KT) {
+            wait_vmcnt<0>();
+            for (int w0 = KT & ~7; w0 < W; w0 += 8) {
+#pragma unroll
+                for (int i = 0; i < FM; i += 2) {
+                    const bool a = w0 + i >= KT, b = w0 + i + 1 >= KT;
+                    if (a)
+                        peer_dma(sP0, w0 >> 3, i);
+                    if (b)
+                        peer_dma(sP1, w0 >> 3, i + 1);
+                    wait_vmcnt<0>();
+                    if (a) {
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] += unpack_bf16x4(
+                                *(const u32x2_t *)(sP0 + wave * PSLOT + pc_off[j]));
+                    }
+                    if (b) {
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i + 1][j] += unpack_bf16x4(
+                                *(const u32x2_t *)(sP1 + wave * PSLOT + pc_off[j]));
+                    }
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slots refill
+                }
+            }
+        }
+
+        // ---- epilogue: bf16 stores, 8 bytes per lane per block ----
+        if (MODE == MODE_RS) {
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out, (uint32_t)p.P * N2);
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws, (uint32_t)p.M * N2);
+            const int s0 = p.rank * p.P;   // first global row of the slice
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = pm_base + 16 * i;
+                const bool in_slice = m >= s0 && m < s0 + p.P;
+                const bool to_ws = !in_slice && m < p.M;
+                const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn_base * 2u;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const bool ok = pn_base + 16 * j < p.N;
+                    const u32x2_t v = pack_bf16x4(acc[i][j]);
+                    store8(ro, (ok && in_slice) ? rbase + 32u * j : OOB, v);
+                    store8(rw, (ok && to_ws) ? rbase + 32u * j : OOB, v);
+                }
+            }
+        } else {
+            uint16_t *ob = p.out + (MODE == MODE_AG ? (size_t)q * p.M * p.N : 0);
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)p.M * N2);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = pm_base + 16 * i;
+                const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn_base * 2u;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const bool ok = m < p.M && pn_base + 16 * j < p.N;
+                    store8(ro, ok ? rbase + 32u * j : OOB, pack_bf16x4(acc[i][j]));
+                }
+            }
+        }
     }
 }
 

@@ -60,11 +60,14 @@ int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64
     return GC_OK;
 }
 
-template <int BM, int BN, int MODE>
-int launch(gc::Args &a, hipStream_t stream, int dev)
+template <int MODE>
+int dispatch(gc::Args &a, hipStream_t stream)
 {
-    a.tiles_m = (a.m_rows + BM - 1) / BM;
-    a.tiles_n = (a.N + BN - 1) / BN;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GC_EIO;
+    a.tiles_m = (a.m_rows + gc::BM - 1) / gc::BM;
+    a.tiles_n = (a.N + gc::BN - 1) / gc::BN;
     const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
     const int64_t total = MODE == gc::MODE_AG ? per * a.R : per;
     if (total > INT32_MAX)
@@ -73,18 +76,12 @@ int launch(gc::Args &a, hipStream_t stream, int dev)
     a.group_m = 4;
     if (a.num_tiles == 0)
         return GC_OK;
-    const int grid = a.num_tiles < cu_count(dev) ? a.num_tiles : cu_count(dev);
-    hipLaunchKernelGGL((gc::gc_kernel<BM, BN, MODE>), dim3(grid), dim3(256), 0, stream, a);
+    // One 256-thread workgroup per CU (the kernel holds 128 KiB of LDS);
+    // a persistent workgroup walks its tiles round by round.
+    const int cus = cu_count(dev);
+    const int grid = a.num_tiles < cus ? a.num_tiles : cus;
+    hipLaunchKernelGGL((gc::gc_kernel<MODE>), dim3(grid), dim3(gc::NT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
-}
-
-template <int MODE>
-int dispatch(gc::Args &a, hipStream_t stream)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return GC_EIO;
-    return launch<256, 256, MODE>(a, stream, dev);
 }
 
 }  // namespace
