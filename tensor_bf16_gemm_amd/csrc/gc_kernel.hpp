@@ -11,22 +11,24 @@
 //  under its component breakdown table about one GEMM kernel that waits
 //  inside the kernel.)
 //
-// Tile: 256 x 256 outputs per workgroup, K in steps of 64, four waves in a
-// 2 x 2 grid, each wave owning 128 x 128 outputs as 8 x 8 blocks of
-// v_mfma_f32_16x16x32_bf16.
+// Tile: 256 x 256 outputs per workgroup of eight waves (two per SIMD) in a
+// 2 (m) x 4 (n) grid; each wave owns 128 x 64 outputs as 8 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16.  K advances 32 per step through a ring of four
+// LDS stages (16 KiB of A + 16 KiB of B each), so the loads of a stage are
+// issued three steps before it is consumed.
 //
-// Operand staging (two LDS stages of 64 KiB):
-//   A tile  [256 m][64 k]  128 B per row; 16-byte chunk c of row m is stored
-//           at chunk c ^ ((m/2) % 8), so the 16 lanes of a ds_read_b128
-//           phase cover all 64 banks.
-//   B tile  [64 k][256 n]  512 B per row (B is N-contiguous and stays so);
-//           32-byte chunk q of row k is stored at q ^ f(k) with
-//           f(k) = (k % 4) + 4 * ((k / 8) % 2), so the 32 lanes of a
-//           ds_read_b64_tr_b16 pass cover all 64 banks.
-// Both tiles move global -> LDS with 16-byte buffer loads that write LDS
-// directly (no VGPR staging); each wave instruction fills 1 KiB of LDS in
-// lane order, so the swizzle is applied by choosing which global chunk each
-// lane fetches.  Loads past M, N or K return zeros (buffer range check).
+// Operand staging:
+//   A stage  [256 m][32 k]  64 B per row; 16-byte chunk c of row m is stored
+//            at chunk c ^ ((m/4) % 4), so the 16 lanes of a ds_read_b128
+//            pass cover all 64 banks.
+//   B stage  [32 k][256 n]  512 B per row (B is N-contiguous and stays so);
+//            32-byte chunk q of row k is stored at q ^ f(k) with
+//            f(k) = (k % 4) + 4 * ((k / 8) % 2), so the 32 lanes of a
+//            ds_read_b64_tr_b16 pass cover all 64 banks.
+// Both move global -> LDS with 16-byte buffer loads that write LDS directly
+// (no VGPR staging); each wave instruction fills 1 KiB of LDS in lane order,
+// so the swizzle is applied by choosing which global chunk each lane
+// fetches.  Loads past M, N or K return zeros (buffer range check).
 //
 // Fragments: the MFMA's first operand is B^T (n rows, 8 consecutive k per
 // lane), read with two ds_read_b64_tr_b16 per block: within each 16-lane
@@ -39,10 +41,10 @@
 //
 // Peer partials (AR, RS): the R-1 peer tiles are added into the fp32
 // accumulators while the K loop runs.  Item w = (peer w/8, row block w%8)
-// is loaded (8 x 8-byte buffer loads per lane) at K-step w-2 and added at
-// K-step w, so the peer traffic streams behind the MFMA work instead of
-// forming an epilogue; items beyond the K loop are added after it, eight
-// items per round trip.
+// is the wave's 16 x 64 block of that peer; it is loaded into one of two
+// LDS slots of the wave at step w-2 and added at step w, so the peer traffic
+// streams behind the MFMA work; items the K loop does not reach are added
+// after it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,12 +84,15 @@ struct Args {
     int group_m;               // row tiles per L2 group
 };
 
-constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+constexpr int BM = 256, BN = 256, BK = 32, NT = 512;
 constexpr int WAVES = NT / 64;             // 8: 2 (m) x 4 (n)
 constexpr int WM = 128, WN = 64, FM = 8, FN = 4;
-constexpr int A_BYTES = BM * BK * 2;       // 32 KiB
-constexpr int B_BYTES = BK * BN * 2;       // 32 KiB
+constexpr int STAGES = 4;
+constexpr int A_BYTES = BM * BK * 2;       // 16 KiB per stage
+constexpr int B_BYTES = BK * BN * 2;       // 16 KiB per stage
 constexpr int PSLOT = 16 * WN * 2;         // one peer block of a wave: 2 KiB
+// Loads a wave issues per step: stage DMA (2 of A + 2 of B) and peer item (2).
+constexpr int DMA_PER_STEP = 4, PEER_PER_ITEM = 2;
 
 // Out-of-range offset for buffer accesses: every buffer addressed here is
 // < 2 GiB, so this offset is past num_records; loads return 0, stores drop.
@@ -100,23 +105,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
                                              BUFFER_FLAGS);
 }
 
-// 16 bytes global -> LDS at lds_base + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_void_t *lds_base, uint32_t off)
+// Buffer resource for the loads below: base, num_records, raw 32-bit format.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t make_rsrc4(const void *p, uint32_t bytes)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (int)off, 0, 0, 0);
+    const uint64_t a = (uint64_t)p;
+    return (u32x4_t){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)BUFFER_FLAGS};
 }
 
-// 8-byte buffer load / store; `soff` is a wave-uniform byte offset added by
-// the hardware (an SGPR), so one VGPR offset serves several columns.
-__device__ __forceinline__ u32x2_t load8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0)
+// LDS byte address of a __shared__ object, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0);
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v,
-                                       uint32_t soff = 0)
+// 16 bytes global -> LDS at lds + 16 * lane.  Issued as inline assembly so
+// that the compiler does not track it: the loop below knows exactly how many
+// of these are in flight and waits for them itself (wait_vmcnt), where the
+// compiler's own tracking of LDS-DMA loads would wait for nearly all of them.
+// M0 is written here only; on gfx950 no other code relies on its value.
+__device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds, uint32_t off)
 {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, (int)soff, 0);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(off), "s"(r)
+                 : "memory");
+}
+
+// 8-byte buffer store.
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
 
 // fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
@@ -139,11 +158,18 @@ __device__ __forceinline__ f32x4_t unpack_bf16x4(u32x2_t w)
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// (Inline assembly with a memory clobber, so that no LDS access moves
+// across it.)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 }
 
 // Workgroup barrier without the compiler's implicit "vmcnt(0)" that a
@@ -169,12 +195,14 @@ template <int MODE>
 __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
     // One array per operand and stage: distinct LDS objects carry distinct
-    // alias scopes, so the compiler knows the loads filling stage s+1 cannot
-    // alias the fragment reads of stage s and does not wait for them.
-    __shared__ __attribute__((aligned(16))) uint8_t sA0[A_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t sB0[B_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t sA1[A_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t sB1[B_BYTES];
+    // alias scopes, so the compiler knows that the loads filling one stage
+    // cannot alias the fragment reads of another and does not wait for them.
+    // (Few enough objects that the compiler's per-object tracking of LDS-DMA
+    // loads stays exact.)  Each stage holds A then B.
+    __shared__ __attribute__((aligned(16))) uint8_t sS0[A_BYTES + B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sS1[A_BYTES + B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sS2[A_BYTES + B_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sS3[A_BYTES + B_BYTES];
     // Peer staging (AR / RS): two slots of one 16 x 64 bf16 block per wave.
     __shared__ __attribute__((aligned(16))) uint8_t sP0[WAVES * PSLOT];
     __shared__ __attribute__((aligned(16))) uint8_t sP1[WAVES * PSLOT];
@@ -189,30 +217,27 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
     const int KT = (p.K + BK - 1) / BK;
     const uint32_t N2 = (uint32_t)p.N * 2u;
 
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B, (uint32_t)p.K * N2);
+    const u32x4_t rB = make_rsrc4(p.B, (uint32_t)p.K * N2);
 
     // ---- per-lane constants -------------------------------------------------
-    // A loader: wave instruction j (0..3) fills LDS rows 32*wave + 8*j + lane/8
-    // (128 B each); the lane's stored chunk lane%8 holds logical chunk
-    // (lane%8) ^ ((row/2)%8) = (lane%8) ^ ((4*j + lane/16) % 8).
-    const int a_c_even = (lane & 7) ^ ((lane >> 4) & 7);          // j even
-    const int a_c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);     // j odd
-    // B loader: wave instruction j (0..3) fills LDS rows k = 8*wave + 2*j +
+    // A loader: wave instruction j (0..1) fills LDS rows 16*(2*wave+j) +
+    // lane/4 (64 B each); the lane's stored chunk lane%4 holds logical chunk
+    // (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
+    const int a_c = (lane & 3) ^ (lane >> 4);
+    // B loader: wave instruction j (0..1) fills LDS rows k = 4*wave + 2*j +
     // lane/32 (512 B each); the lane's stored 16-byte slot lane%32 is half
-    // lane%2 of stored 32-byte chunk (lane%32)/2 = logical chunk ^ f(k), with
-    // f(k) = (k%4) + 4*((k/8)%2) = ((2*j + lane/32) % 4) + 4*(wave%2).
+    // lane%2 of stored 32-byte chunk (lane%32)/2 = logical chunk ^ f(k).
     const int b_slot = lane & 31;
     // fragment reads
     const int fi = lane & 15, fg = lane >> 4;
-    const uint32_t a_frag0 = (uint32_t)(wm * WM * 128 + fi * 128 + ((0 + fg) ^ (fi >> 1)) * 16);
-    const uint32_t a_frag1 = (uint32_t)(wm * WM * 128 + fi * 128 + ((4 + fg) ^ (fi >> 1)) * 16);
+    const uint32_t a_frag = (uint32_t)(wm * WM * 64 + fi * 64 + ((fg ^ (fi >> 2)) << 4));
     const int fB = (fi >> 2) | ((fg & 1) << 2);
     // B^T block j of this wave is logical 32-byte chunk q = 4*wn + j.
-    const uint32_t b_frag = (uint32_t)((8 * fg + (fi >> 2)) * 512 + (wn >> 1) * 256 + 8 * (fi & 3));
     uint32_t b_frag_j[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-        b_frag_j[j] = b_frag + (uint32_t)(((4 * (wn & 1) + j) ^ fB) * 32);
+        b_frag_j[j] = (uint32_t)((8 * fg + (fi >> 2)) * 512 + (wn >> 1) * 256 + 8 * (fi & 3) +
+                                 (((4 * (wn & 1) + j) ^ fB) * 32));
 
     for (int round = 0;; ++round) {
         const int lin = round * G;
@@ -240,7 +265,10 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int nt = in_g / gh;
         const int m0 = mt * BM, n0 = nt * BN;
 
-        __syncthreads();  // LDS of the previous tile is no longer read
+        // Every load of the previous tile has landed and every wave is done
+        // reading its LDS stages before this tile's loads reuse them.
+        wait_vmcnt<0>();
+        barrier_only();
 
         const uint16_t *Asrc = p.A;
         int q = 0;
@@ -275,57 +303,48 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     continue;
             }
         }
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(Asrc, (uint32_t)p.M * (uint32_t)p.K * 2u);
+        const u32x4_t rA = make_rsrc4(Asrc, (uint32_t)p.M * (uint32_t)p.K * 2u);
 
         // ---- loader offsets for this tile at k0 = 0 (rows past M and
         // columns past N already folded into OOB); a step adds its k0 ----
-        uint32_t a_off[4], b_off[4];
-        int a_kc[4], b_k[4];
+        uint32_t a_off[2], b_off[2];
+        int b_k[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = m0 + 32 * wave + 8 * j + (lane >> 3);
-            const int c = (j & 1) ? a_c_odd : a_c_even;
-            a_kc[j] = 8 * c;
-            a_off[j] = row < p.M ? ((uint32_t)row * (uint32_t)p.K + (uint32_t)(8 * c)) * 2u : OOB;
-            const int k = 8 * wave + 2 * j + (lane >> 5);
+        for (int j = 0; j < 2; ++j) {
+            const int row = m0 + 16 * (2 * wave + j) + (lane >> 2);
+            a_off[j] = row < p.M ? ((uint32_t)row * (uint32_t)p.K + (uint32_t)(8 * a_c)) * 2u : OOB;
+            const int k = 4 * wave + 2 * j + (lane >> 5);
             const int fk = (k & 3) | (((k >> 3) & 1) << 2);
             const int n = n0 + 16 * ((b_slot >> 1) ^ fk) + 8 * (b_slot & 1);
             b_k[j] = k;
             b_off[j] = n < p.N ? ((uint32_t)k * (uint32_t)p.N + (uint32_t)n) * 2u : OOB;
         }
-        auto dma_stage = [&](int kt, uint8_t *sa, uint8_t *sb) {
+        // Loads of stage kt into (sa, sb).  Steps past the K loop issue the
+        // same number of loads, all out of range, so that the wait counts of
+        // the loop stay constant.
+        auto dma_stage = [&](int kt, const uint8_t *sa, const uint8_t *sb) {
             const int k0 = kt * BK;
             const uint32_t ka = (uint32_t)k0 * 2u, kb = (uint32_t)k0 * N2;
+            const uint32_t la = lds_addr(sa) + (uint32_t)(16 * (2 * wave) * 64);
+            const uint32_t lb = lds_addr(sb) + (uint32_t)((4 * wave) * 512);
             if (k0 + BK <= p.K) {   // whole step inside K: no per-lane K test
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dma16(rA, (lds_void_t *)(sa + (32 * wave + 8 * j) * 128), a_off[j] + ka);
+                for (int j = 0; j < 2; ++j)
+                    dma16(rA, la + j * 1024, a_off[j] + ka);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dma16(rB, (lds_void_t *)(sb + (8 * wave + 2 * j) * 512), b_off[j] + kb);
+                for (int j = 0; j < 2; ++j)
+                    dma16(rB, lb + j * 1024, b_off[j] + kb);
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dma16(rA, (lds_void_t *)(sa + (32 * wave + 8 * j) * 128),
-                          k0 + a_kc[j] < p.K ? a_off[j] + ka : OOB);
+                for (int j = 0; j < 2; ++j)
+                    dma16(rA, la + j * 1024, k0 + 8 * a_c < p.K ? a_off[j] + ka : OOB);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    dma16(rB, (lds_void_t *)(sb + (8 * wave + 2 * j) * 512),
-                          k0 + b_k[j] < p.K ? b_off[j] + kb : OOB);
+                for (int j = 0; j < 2; ++j)
+                    dma16(rB, lb + j * 1024, k0 + b_k[j] < p.K ? b_off[j] + kb : OOB);
             }
         };
 
         // ---- peer items (AR / RS) ----
-        // Rows of this wave's blocks: m = m0 + wm*128 + 16*i + lane%16;
-        // columns n = n0 + wn*64 + 16*j + 4*(lane/16).  Peer rows outside
-        // [row_lo, row_hi) read as zero through the buffer range check.
-        const int pm_base = m0 + wm * WM + fi;
-        const int pn_base = n0 + wn * WN + 4 * fg;
-        const int row_lo = MODE == MODE_RS ? p.lo : 0;
-        const int row_hi = MODE == MODE_RS ? p.hi : p.M;
-        int W = 0;
-        if (PEERS && m0 < row_hi && m0 + BM > row_lo)
-            W = p.npeers * FM;
         // Item (peer pp, row block i) is the wave's 16 x 64 block of that
         // peer partial: rows blk .. blk+15 (blk = m0 + 128*wm + 16*i), columns
         // n0 + 64*wn .. +63.  It moves global -> LDS with two 16-byte DMA
@@ -333,28 +352,36 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // block row r is stored at chunk c ^ ((r/2) % 8).  The buffer starts
         // at the first row that may be read (>= row_lo) and ends at row_hi,
         // so rows outside [row_lo, row_hi) read as zero (rows below wrap past
-        // 2^31); chunks past N are masked per lane on edge tiles.
+        // 2^31); chunks past N are masked per lane on edge tiles.  Items
+        // outside [0, W) load nothing (an empty buffer).
+        const int pm_base = m0 + wm * WM + fi;
+        const int pn_base = n0 + wn * WN + 4 * fg;
+        const int row_lo = MODE == MODE_RS ? p.lo : 0;
+        const int row_hi = MODE == MODE_RS ? p.hi : p.M;
+        int W = 0;
+        if (PEERS && m0 < row_hi && m0 + BM > row_lo)
+            W = p.npeers * FM;
         uint32_t pd_off[2];
-        bool pd_ok[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int row = 8 * r + (lane >> 3);
             const int c = (lane & 7) ^ ((row >> 1) & 7);
             const int n = n0 + wn * WN + 8 * c;
-            pd_off[r] = (uint32_t)row * N2 + (uint32_t)n * 2u;
-            pd_ok[r] = n < p.N;
+            pd_off[r] = n < p.N ? (uint32_t)row * N2 + (uint32_t)n * 2u : OOB;
         }
-        auto peer_dma = [&](uint8_t *slotbuf, int pp, int i) {
+        auto peer_dma = [&](const uint8_t *slotbuf, int w, int i) {
+            const bool live_item = w >= 0 && w < W;
+            const int pp = live_item ? (w >> 3) : 0;
             const int blk = m0 + wm * WM + 16 * i;
             const int start = max(blk, row_lo);
-            const int rows = max(row_hi - start, 0);
-            const __amdgpu_buffer_rsrc_t rp = make_rsrc(
+            const int rows = live_item ? max(row_hi - start, 0) : 0;
+            const u32x4_t rp = make_rsrc4(
                 p.partials + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
             const uint32_t shift = (uint32_t)(start - blk) * N2;
+            const uint32_t ls = lds_addr(slotbuf) + (uint32_t)(wave * PSLOT);
 #pragma unroll
             for (int r = 0; r < 2; ++r)
-                dma16(rp, (lds_void_t *)(slotbuf + wave * PSLOT + r * 1024),
-                      pd_ok[r] ? pd_off[r] - shift : OOB);
+                dma16(rp, ls + r * 1024, pd_off[r] == OOB ? OOB : pd_off[r] - shift);
         };
         // Reading back: lane (fi, fg) needs row fi, columns 16*j + 4*fg .. +3,
         // i.e. half fg%2 of logical chunk 2*j + fg/2.
@@ -371,21 +398,20 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-        auto half_step = [&](const uint8_t *cA, const uint8_t *cB, int ks) {
-            bf16x8_t fa[FN], fb[FM];
+        auto read_frags = [&](const uint8_t *cA, const uint8_t *cB, bf16x8_t (&fa)[FN],
+                              bf16x8_t (&fb)[FM]) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const uint8_t *base = cB + b_frag_j[j] + ks * 32 * 512;
+                const uint8_t *base = cB + b_frag_j[j];
                 bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
                 bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * 512));
                 fa[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                fb[i] = *(const bf16x8_t *)(cA + (ks ? a_frag1 : a_frag0) + i * 16 * 128);
-            // All twelve fragments are requested before the first MFMA, so
-            // their LDS latency overlaps instead of being paid per fragment.
-            __builtin_amdgcn_sched_barrier(0);
+                fb[i] = *(const bf16x8_t *)(cA + a_frag + i * 16 * 64);
+        };
+        auto mfmas = [&](const bf16x8_t (&fa)[FN], const bf16x8_t (&fb)[FM]) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -393,54 +419,67 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
         };
 
-        // prologue: item 0, stage 0, item 1  (the order the steps rely on)
-        if (PEERS && W > 0)
+        // Prologue: virtual steps -3, -2, -1 issue stages 0, 1, 2 and peer
+        // items -1 (nothing), 0, 1, exactly as a loop step would.
+        dma_stage(0, sS0, sS0 + A_BYTES);
+        if (PEERS)
+            peer_dma(sP1, -1, 7);
+        dma_stage(1, sS1, sS1 + A_BYTES);
+        if (PEERS)
             peer_dma(sP0, 0, 0);
-        if (KT > 0)
-            dma_stage(0, sA0, sB0);
-        if (PEERS && W > 1)
-            peer_dma(sP1, 0, 1);
+        dma_stage(2, sS2, sS2 + A_BYTES);
+        if (PEERS)
+            peer_dma(sP1, 1, 1);
 
         // ---- main loop, unrolled by 8 so that the stage, the peer slot and
-        // the peer row block are compile-time constants.  Step kt: wait for
-        // the own loads of stage kt (only peer item kt+1 may still fly);
-        // barrier (everyone's stage kt landed, everyone done reading stage
-        // kt-1); loads of stage kt+1; add peer item kt and load item kt+2;
-        // MFMAs of stage kt. ----
+        // the peer row block are compile-time constants.  Step kt:
+        //   wait for the own loads of stage kt (the loads issued after them
+        //   -- stages kt+1, kt+2 and peer items kt-1 .. kt+1 -- may fly);
+        //   barrier (everyone's stage kt landed, everyone done with kt-1);
+        //   loads of stage kt+3 into kt-1's buffers; add peer item kt (the
+        //   compiler waits for its slot's loads) and load item kt+2; MFMAs
+        //   of stage kt. ----
+        constexpr int AFTER = 2 * DMA_PER_STEP + (PEERS ? 3 * PEER_PER_ITEM : 0);
         for (int kt0 = 0; kt0 < KT; kt0 += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int kt = kt0 + u;
                 if (kt < KT) {
-                    uint8_t *cA = (u & 1) ? sA1 : sA0;
-                    uint8_t *cB = (u & 1) ? sB1 : sB0;
-                    uint8_t *nA = (u & 1) ? sA0 : sA1;
-                    uint8_t *nB = (u & 1) ? sB0 : sB1;
+                    uint8_t *cS = (u & 3) == 0 ? sS0 : (u & 3) == 1 ? sS1 : (u & 3) == 2 ? sS2 : sS3;
+                    uint8_t *nS = (u & 3) == 0 ? sS3 : (u & 3) == 1 ? sS0 : (u & 3) == 2 ? sS1 : sS2;
+                    uint8_t *cA = cS, *cB = cS + A_BYTES, *nA = nS, *nB = nS + A_BYTES;
                     uint8_t *sl = (u & 1) ? sP1 : sP0;
-                    if (PEERS && kt + 1 < W)
-                        wait_vmcnt<2>();
-                    else
-                        wait_vmcnt<0>();
+                    wait_vmcnt<AFTER>();
                     barrier_only();
-                    if (kt + 1 < KT)
-                        dma_stage(kt + 1, nA, nB);
+                    // Fragment reads go first: their LDS latency is covered by
+                    // the load issue and the peer add that follow.
+                    bf16x8_t fa[FN], fb[FM];
+                    read_frags(cA, cB, fa, fb);
+                    dma_stage(kt + 3, nA, nB);
                     if (PEERS) {
+                        // Item kt was issued at step kt-2; after it came stage
+                        // kt+2, item kt+1 and stage kt+3.
+                        wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
                         if (kt < W) {
+                            u32x2_t pv[FN];
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
-                                acc[u][j] += unpack_bf16x4(
-                                    *(const u32x2_t *)(sl + wave * PSLOT + pc_off[j]));
+                                pv[j] = *(const u32x2_t *)(sl + wave * PSLOT + pc_off[j]);
+#pragma unroll
+                            for (int j = 0; j < FN; ++j)
+                                acc[u][j] += unpack_bf16x4(pv[j]);
                         }
-                        if (kt + 2 < W)
-                            peer_dma(sl, (kt + 2) >> 3, (u + 2) & 7);
                     }
-                    half_step(cA, cB, 0);
-                    half_step(cA, cB, 1);
+                    mfmas(fa, fb);
+                    if (PEERS) {
+                        wait_lgkmcnt0();  // slot read back before it is refilled
+                        peer_dma(sl, kt + 2, (u + 2) & 7);
+                    }
                 }
             }
         }
 
-        // ---- peer items the K loop did not reach: two in flight ----
+        // ---- peer items the K loop did not reach: two per round trip ----
         if (PEERS && W > KT) {
             wait_vmcnt<0>();
             for (int w0 = KT & ~7; w0 < W; w0 += 8) {
@@ -448,9 +487,9 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 for (int i = 0; i < FM; i += 2) {
                     const bool a = w0 + i >= KT, b = w0 + i + 1 >= KT;
                     if (a)
-                        peer_dma(sP0, w0 >> 3, i);
+                        peer_dma(sP0, w0 + i, i);
                     if (b)
-                        peer_dma(sP1, w0 >> 3, i + 1);
+                        peer_dma(sP1, w0 + i + 1, i + 1);
                     wait_vmcnt<0>();
                     if (a) {
 #pragma unroll
@@ -464,7 +503,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                             acc[i + 1][j] += unpack_bf16x4(
                                 *(const u32x2_t *)(sP1 + wave * PSLOT + pc_off[j]));
                     }
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slots refill
+                    wait_lgkmcnt0();  // reads done before the slots refill
                 }
             }
         }
