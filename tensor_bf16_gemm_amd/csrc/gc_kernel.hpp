@@ -175,9 +175,13 @@ __device__ __forceinline__ void wait_lgkmcnt0()
 // Workgroup barrier without the compiler's implicit "vmcnt(0)" that a
 // __syncthreads() gets while LDS-DMA loads are pending: every caller waits
 // explicitly for exactly the loads the barrier must cover.
+// The scheduling barriers keep every instruction on its side of it, so the
+// phases of the ping-pong schedule below stay where the code puts them.
 __device__ __forceinline__ void barrier_only()
 {
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Logical tile of workgroup `b` in one round of `G` workgroups.  Workgroups
@@ -431,15 +435,26 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         if (PEERS)
             peer_dma(sP1, 1, 1);
 
-        // ---- main loop, unrolled by 8 so that the stage, the peer slot and
-        // the peer row block are compile-time constants.  Step kt:
-        //   wait for the own loads of stage kt (the loads issued after them
-        //   -- stages kt+1, kt+2 and peer items kt-1 .. kt+1 -- may fly);
-        //   barrier (everyone's stage kt landed, everyone done with kt-1);
-        //   loads of stage kt+3 into kt-1's buffers; add peer item kt (the
-        //   compiler waits for its slot's loads) and load item kt+2; MFMAs
-        //   of stage kt. ----
+        // ---- main loop: ping-pong between the two waves of each SIMD ----
+        // Waves 0-3 (group 0) and 4-7 (group 1) sit one per SIMD each.  Step
+        // kt is a memory phase M(kt) -- fragment reads of stage kt, loads of
+        // stage kt+3, peer item kt added and item kt+2 loaded -- then a
+        // compute phase C(kt) of 32 MFMAs.  Group 1 runs one phase behind
+        // group 0, so on every SIMD one wave computes while the other does
+        // its memory phase; a barrier separates phases:
+        //   group 0:  M0 C0 M1 C1 ...      group 1:  -- M0 C0 M1 C1 ...
+        // At the end of M(kt) a wave has its own loads of stage kt+1 done
+        // (the loads after them -- stages kt+2, kt+3, items kt..kt+2 -- may
+        // fly) and its fragment reads of stage kt complete, so after the
+        // next barrier of the other group's M(kt+1)... every stage read is
+        // complete and every stage about to be read has landed.
+        // The loop is unrolled by 8 so that the stage, the peer slot and the
+        // peer row block are compile-time constants.
         constexpr int AFTER = 2 * DMA_PER_STEP + (PEERS ? 3 * PEER_PER_ITEM : 0);
+        const bool lag = wave >= 4;
+        wait_vmcnt<AFTER>();          // own loads of stage 0 done
+        if (lag)
+            barrier_only();
         for (int kt0 = 0; kt0 < KT; kt0 += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -449,15 +464,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     uint8_t *nS = (u & 3) == 0 ? sS3 : (u & 3) == 1 ? sS0 : (u & 3) == 2 ? sS1 : sS2;
                     uint8_t *cA = cS, *cB = cS + A_BYTES, *nA = nS, *nB = nS + A_BYTES;
                     uint8_t *sl = (u & 1) ? sP1 : sP0;
-                    wait_vmcnt<AFTER>();
+                    // ---- M(kt) ----
                     barrier_only();
-                    // Fragment reads go first: their LDS latency is covered by
-                    // the load issue and the peer add that follow.
                     bf16x8_t fa[FN], fb[FM];
                     read_frags(cA, cB, fa, fb);
                     dma_stage(kt + 3, nA, nB);
                     if (PEERS) {
-                        // Item kt was issued at step kt-2; after it came stage
+                        // Item kt was issued in M(kt-2); after it came stage
                         // kt+2, item kt+1 and stage kt+3.
                         wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
                         if (kt < W) {
@@ -469,15 +482,19 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                             for (int j = 0; j < FN; ++j)
                                 acc[u][j] += unpack_bf16x4(pv[j]);
                         }
-                    }
-                    mfmas(fa, fb);
-                    if (PEERS) {
                         wait_lgkmcnt0();  // slot read back before it is refilled
                         peer_dma(sl, kt + 2, (u + 2) & 7);
                     }
+                    wait_vmcnt<AFTER>();  // own loads of stage kt+1 done
+                    wait_lgkmcnt0();      // stage kt fully read into registers
+                    // ---- C(kt) ----
+                    barrier_only();
+                    mfmas(fa, fb);
                 }
             }
         }
+        if (!lag)
+            barrier_only();           // same barrier count in both groups
 
         // ---- peer items the K loop did not reach: two per round trip ----
         if (PEERS && W > KT) {
