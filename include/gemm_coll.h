@@ -33,9 +33,11 @@
  * - R, the tensor-parallel size, must satisfy 1 < R <= 16 and 128 % R == 0,
  *   i.e. R in {2, 4, 8, 16} (the validation chain of maybe_init_gemm_rs_ar,
  *   "[Kimi-K3] Extend GEMM-RS to GEMM-AR", 关键源码片段); 0 <= rank < R.
- * - Ownership: the caller owns every buffer.  The library allocates no device
- *   memory, never synchronizes, and keeps no mutable state besides a per-device
- *   cache of device properties; calls are thread-safe.  Work is enqueued on
+ * - Ownership: the caller owns every buffer, including the optional
+ *   workspace.  The library allocates no device memory, never synchronizes,
+ *   and keeps no mutable state besides a per-device cache of device
+ *   properties and a per-device launch counter; calls are thread-safe (but a
+ *   workspace serves one call at a time).  Work is enqueued on
  *   `stream` (a hipStream_t; NULL = the null stream) and is complete only
  *   when that stream is.  Outputs must not alias any input.
  * - Errors: a negative return means nothing was launched.
@@ -45,6 +47,10 @@
  *                 or more, or a size above INT32_MAX)
  *     GC_EIO      the HIP launch failed
  *   M == 0 (or N == 0) is valid and launches nothing.
+ * - Stream-K time-out: if a workgroup waiting for a partner's partial sum
+ *   gives up (the partner never ran -- only possible if the device could not
+ *   hold all workgroups at once), the tile is left unwritten and, when
+ *   peers->status is not NULL, *status is set to GC_TIMEOUT_BASE + 16.
  */
 #ifndef GEMM_COLL_H
 #define GEMM_COLL_H
@@ -81,11 +87,21 @@ typedef struct gc_peers {
        each call passes a larger epoch.  flags[rank] is not read. */
     const uint32_t *flags;
     uint32_t epoch;
-    /* ag_gemm: device int32, written only on a time-out (see ag_gemm). */
+    /* Device int32, written only on a time-out: required by ag_gemm (see
+       there), optional (may be NULL) for gemm_ar / gemm_rs. */
     int32_t *status;
     /* ag_gemm: polls of one flag before giving up; 0 = the default
        (about one second). */
     uint32_t max_spins;
+    /* All calls, optional: device workspace of at least
+       gemm_coll_workspace_bytes() bytes, zero-filled before its first use
+       and not used by two calls at the same time.  With it, tiles left over
+       after the last full round of workgroups are split along K across all
+       compute units (partial sums exchanged through it); with NULL, every
+       tile is computed whole.  Results agree to rounding of the fp32
+       partial sums. */
+    void *workspace;
+    uint64_t workspace_bytes;
 } gc_peers;
 
 /*
@@ -137,6 +153,10 @@ int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K
  * their unfused GEMM there.  The entry points themselves run any M >= 0.
  */
 int gemm_coll_should_run(int64_t M);
+
+/* Bytes of workspace that lets a call split tiles along K on the current
+ * device (see gc_peers.workspace); negative on a HIP error. */
+int64_t gemm_coll_workspace_bytes(void);
 
 /* Static description of a return code (never NULL). */
 const char *gemm_coll_strerror(int code);

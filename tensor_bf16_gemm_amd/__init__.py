@@ -8,7 +8,10 @@ HIP kernels.  PyTorch supplies device memory and the stream.
     out = gemm_rs(A, B, partials, ws, R=8, rank=5)        # GEMM-RS
     out = ag_gemm(A, B, shards, flags, status, R=8, rank=3, epoch=1)
 
-Tensors are bf16, contiguous, on the current CUDA (HIP) device.  A failed
+Tensors are bf16, contiguous, on the current CUDA (HIP) device.  By default
+each call uses a per-device workspace (allocated once) that lets the kernel
+split leftover tiles along K; pass workspace=False to compute every tile
+whole, or a zero-filled uint8 tensor of workspace_bytes() of your own.  A failed
 call raises RuntimeError with the library's message.  If the library is not
 built, the first call raises: there is no fallback path.
 """
@@ -18,6 +21,7 @@ import ctypes
 import os
 
 __all__ = ["gemm_ar", "gemm_rs", "ag_gemm", "should_run", "strerror", "lib", "GcPeers",
+           "workspace_bytes", "default_workspace",
            "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_TIMEOUT_BASE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm_coll.so")
@@ -39,6 +43,8 @@ class GcPeers(ctypes.Structure):
         ("epoch", ctypes.c_uint32),
         ("status", ctypes.c_void_p),
         ("max_spins", ctypes.c_uint32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -63,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_coll_should_run.restype = ctypes.c_int
         L.gemm_coll_strerror.argtypes = [ctypes.c_int]
         L.gemm_coll_strerror.restype = ctypes.c_char_p
+        L.gemm_coll_workspace_bytes.argtypes = []
+        L.gemm_coll_workspace_bytes.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -74,6 +82,41 @@ def strerror(code: int) -> str:
 def should_run(M: int) -> bool:
     """Dispatch gate: True when the fused path should serve M tokens (M >= 128)."""
     return bool(lib().gemm_coll_should_run(int(M)))
+
+
+_workspaces: dict = {}
+
+
+def workspace_bytes() -> int:
+    """Bytes of workspace that lets calls on the current device split tiles along K."""
+    n = lib().gemm_coll_workspace_bytes()
+    if n < 0:
+        raise RuntimeError(f"gemm_coll_workspace_bytes: {strerror(n)}")
+    return n
+
+
+def default_workspace(device=None):
+    """A zero-filled workspace for `device`, allocated once and reused.  It
+    serves one call at a time: calls on concurrent streams need their own."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else
+                       torch.device(device).index)
+    ws = _workspaces.get(dev.index)
+    if ws is None:
+        with torch.cuda.device(dev):
+            ws = torch.zeros(workspace_bytes(), dtype=torch.uint8, device=dev)
+        _workspaces[dev.index] = ws
+    return ws
+
+
+def _ws_fields(workspace, device):
+    """(pointer, bytes) for gc_peers: workspace=None -> the default one,
+    False -> none (every tile computed whole), else a uint8 device tensor."""
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        workspace = default_workspace(device)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _check(code: int, what: str):
@@ -104,7 +147,8 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None):
+def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None, workspace=None,
+            status=None):
     """GEMM-AR: out [M,N] = bf16(A.B + sum of partials [R-1,M,N])."""
     import torch
     M, K = A.shape
@@ -115,13 +159,16 @@ def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (M, N))
-    peers = GcPeers(partials=_ptr(partials))
+    wp, wb = _ws_fields(workspace, A.device)
+    peers = GcPeers(partials=_ptr(partials), workspace=wp, workspace_bytes=wb,
+                    status=_ptr(status))
     _check(lib().gemm_ar(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_ar")
     return out
 
 
-def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None):
+def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None, workspace=None,
+            status=None):
     """GEMM-RS: out [ceil(M/R), N] = this rank's rows of bf16(A.B + sum of partials);
     ws [M,N] receives bf16(A.B) on the rows this rank does not own."""
     import torch
@@ -135,14 +182,16 @@ def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None):
     if out is None:
         out = torch.empty((P, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (P, N))
-    peers = GcPeers(partials=_ptr(partials), ws=_ptr(ws))
+    wp, wb = _ws_fields(workspace, A.device)
+    peers = GcPeers(partials=_ptr(partials), ws=_ptr(ws), workspace=wp, workspace_bytes=wb,
+                    status=_ptr(status))
     _check(lib().gemm_rs(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_rs")
     return out
 
 
 def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: int,
-            max_spins: int = 0, stream=None):
+            max_spins: int = 0, stream=None, workspace=None):
     """AG-GEMM: out [R*Ms, N] = bf16(concat(shards).B), A = this rank's shard [Ms,K].
     flags: int32 tensor [R] in device memory or pinned host memory (the kernel
     polls it with system-scope loads); status: int32 device tensor [1]."""
@@ -160,8 +209,10 @@ def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: 
     if out is None:
         out = torch.empty((R * Ms, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (R * Ms, N))
+    wp, wb = _ws_fields(workspace, A.device)
     peers = GcPeers(shards=_ptr(shards), flags=_ptr(flags), epoch=int(epoch) & 0xFFFFFFFF,
-                    status=_ptr(status), max_spins=int(max_spins))
+                    status=_ptr(status), max_spins=int(max_spins), workspace=wp,
+                    workspace_bytes=wb)
     _check(lib().ag_gemm(_ptr(A), _ptr(B), Ms, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "ag_gemm")
     return out

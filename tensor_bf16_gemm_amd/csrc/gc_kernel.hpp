@@ -82,6 +82,19 @@ struct Args {
     int tiles_m, tiles_n;      // per shard for AG
     int num_tiles;             // total (AG: R * tiles_m * tiles_n)
     int group_m;               // row tiles per L2 group
+    // Work split.  The first dp_tiles tiles are taken whole, round by round;
+    // the remaining sk_tiles are split along K ("stream-K"): their K-steps
+    // (kt8 per tile, the step count rounded up to a multiple of 8) are cut
+    // into consecutive runs of sk_iters steps, one run per workgroup.  A tile
+    // shared by several workgroups is finished by the one holding its first
+    // step (the owner); the others leave fp32 partials in sk_part and raise
+    // sk_flags[v] to sk_epoch.
+    int dp_tiles;
+    int sk_tiles, kt8, sk_iters;
+    uint32_t *sk_flags;        // [gridDim.x]
+    float *sk_part;            // [gridDim.x][BM*BN]
+    uint32_t sk_epoch;
+    uint32_t sk_max_spins;
 };
 
 constexpr int BM = 256, BN = 256, BK = 32, NT = 512;
@@ -93,11 +106,15 @@ constexpr int B_BYTES = BK * BN * 2;       // 16 KiB per stage
 constexpr int PSLOT = 16 * WN * 2;         // one peer block of a wave: 2 KiB
 // Loads a wave issues per step: stage DMA (2 of A + 2 of B) and peer item (2).
 constexpr int DMA_PER_STEP = 4, PEER_PER_ITEM = 2;
+constexpr int PART_FLOATS = BM * BN;       // one fp32 partial tile
 
 // Out-of-range offset for buffer accesses: every buffer addressed here is
 // < 2 GiB, so this offset is past num_records; loads return 0, stores drop.
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int BUFFER_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
+// Cache policy of a buffer access: sc0 | sc1 (system coherent: a store writes
+// through to memory, a load misses every cache).
+constexpr int CPOL_SYS = 1 | 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -111,6 +128,29 @@ __device__ __forceinline__ u32x4_t make_rsrc4(const void *p, uint32_t bytes)
 {
     const uint64_t a = (uint64_t)p;
     return (u32x4_t){(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, (uint32_t)BUFFER_FLAGS};
+}
+
+// A wave-uniform value the compiler may not fold or hoist (an empty asm that
+// claims to change it).  LDS addresses built from it are formed where they
+// are used instead of being kept in registers for every unrolled step.
+__device__ __forceinline__ uint32_t opaque(uint32_t x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// The same for a per-lane value: code after the K loop recomputes its lane
+// offsets from this instead of keeping the loop's copies alive through it.
+__device__ __forceinline__ int opaque_v(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T *lds_ptr(uint32_t a)
+{
+    return (const __attribute__((address_space(3))) T *)(uintptr_t)a;
 }
 
 // LDS byte address of a __shared__ object, as a wave-uniform value.
@@ -243,14 +283,41 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         b_frag_j[j] = (uint32_t)((8 * fg + (fi >> 2)) * 512 + (wn >> 1) * 256 + 8 * (fi & 3) +
                                  (((4 * (wn & 1) + j) ^ fB) * 32));
 
-    for (int round = 0;; ++round) {
-        const int lin = round * G;
-        if (lin >= p.num_tiles)
+    // Work list of this workgroup: whole tiles round by round, then its run
+    // of stream-K steps, cut at tile boundaries into segments [g0, g1).
+    const int v = xcd_remap(blockIdx.x, G);    // position in stream-K order
+    int dp_lin = 0;                            // first tile of the next whole-tile round
+    const int sk_total = p.sk_tiles * p.kt8;
+    // Runs are laid out from the end of the stream-K steps: workgroup v
+    // takes [S - (v+1)*sk_iters, S - v*sk_iters), so a tile's first steps
+    // belong to the higher v (its owner), which waits only for lower v.
+    int it = max(sk_total - (v + 1) * p.sk_iters, 0);
+    const int it_end = max(sk_total - v * p.sk_iters, 0);
+    for (;;) {
+        int L, g0, g1;
+        if (dp_lin < p.dp_tiles) {
+            const int lin = dp_lin;
+            const int live = min(G, p.dp_tiles - lin);
+            dp_lin = live < G ? p.dp_tiles : lin + G;   // no overflow past dp_tiles
+            if ((int)blockIdx.x >= live)
+                continue;                      // idle in this last, partial round
+            L = lin + xcd_remap(blockIdx.x, live);
+            g0 = 0;
+            g1 = KT;
+        } else if (it < it_end) {
+            const int tt = it / p.kt8;
+            g0 = it - tt * p.kt8;
+            const int seg_end = min(it_end, (tt + 1) * p.kt8);
+            g1 = min(KT, g0 + (seg_end - it));
+            it = seg_end;
+            L = p.dp_tiles + tt;
+            if (g0 >= KT)
+                continue;                      // only padding steps of the tile
+        } else {
             break;
-        const int live = min(G, p.num_tiles - lin);
-        if ((int)blockIdx.x >= live)
-            break;
-        const int L = lin + xcd_remap(blockIdx.x, live);
+        }
+        const bool contrib = g0 > 0;           // partial for an owner elsewhere
+        const bool owner = g0 == 0 && g1 < KT; // collects partials after its run
 
         // Tile: shard step s (AG), row tile mt, column tile nt, grouped
         // column-major over `group_m` row tiles for L2 reuse.
@@ -269,10 +336,32 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int nt = in_g / gh;
         const int m0 = mt * BM, n0 = nt * BN;
 
-        // Every load of the previous tile has landed and every wave is done
-        // reading its LDS stages before this tile's loads reuse them.
+        // Every load of the previous segment has landed and every wave is
+        // done reading its LDS stages before this segment's loads reuse them.
         wait_vmcnt<0>();
         barrier_only();
+
+        // Raise this workgroup's partial-ready flag (after its partial, if
+        // any, is stored and written back).
+        // Flags are two words per workgroup: [2v] the epoch of its last
+        // hand-over, [2v+1] whether that partial is valid.  Partials and
+        // flags move with system-coherent accesses (sc0 sc1: stores write
+        // through, loads miss the L2), so handing one over needs no L2
+        // write-back or invalidation, which would evict the A and B tiles
+        // every other workgroup of the XCD is using.  Order: every store of
+        // the partial completed (vmcnt 0 in every wave), then the valid word,
+        // then the epoch word.
+        auto signal_partial = [&](uint32_t ok) {
+            wait_vmcnt<0>();
+            barrier_only();
+            if (tid == 0) {
+                __hip_atomic_store(p.sk_flags + 2 * v + 1, ok, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+                wait_vmcnt<0>();
+                __hip_atomic_store(p.sk_flags + 2 * v, p.sk_epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        };
 
         const uint16_t *Asrc = p.A;
         int q = 0;
@@ -303,8 +392,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 __syncthreads();
                 const int ok = s_ready;
                 __syncthreads();
-                if (!ok)
+                if (!ok) {
+                    if (contrib)
+                        signal_partial(0u);  // the owner must not wait forever
                     continue;
+                }
             }
         }
         const u32x4_t rA = make_rsrc4(Asrc, (uint32_t)p.M * (uint32_t)p.K * 2u);
@@ -312,7 +404,6 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // ---- loader offsets for this tile at k0 = 0 (rows past M and
         // columns past N already folded into OOB); a step adds its k0 ----
         uint32_t a_off[2], b_off[2];
-        int b_k[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = m0 + 16 * (2 * wave + j) + (lane >> 2);
@@ -320,18 +411,26 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const int k = 4 * wave + 2 * j + (lane >> 5);
             const int fk = (k & 3) | (((k >> 3) & 1) << 2);
             const int n = n0 + 16 * ((b_slot >> 1) ^ fk) + 8 * (b_slot & 1);
-            b_k[j] = k;
             b_off[j] = n < p.N ? ((uint32_t)k * (uint32_t)p.N + (uint32_t)n) * 2u : OOB;
         }
         // Loads of stage kt into (sa, sb).  Steps past the K loop issue the
         // same number of loads, all out of range, so that the wait counts of
         // the loop stay constant.
+        // Steps at or past g1 (the end of this segment) issue the same number
+        // of loads, all out of range.
         auto dma_stage = [&](int kt, const uint8_t *sa, const uint8_t *sb) {
             const int k0 = kt * BK;
             const uint32_t ka = (uint32_t)k0 * 2u, kb = (uint32_t)k0 * N2;
             const uint32_t la = lds_addr(sa) + (uint32_t)(16 * (2 * wave) * 64);
             const uint32_t lb = lds_addr(sb) + (uint32_t)((4 * wave) * 512);
-            if (k0 + BK <= p.K) {   // whole step inside K: no per-lane K test
+            if (kt >= g1) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    dma16(rA, la + j * 1024, OOB);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    dma16(rB, lb + j * 1024, OOB);
+            } else if (k0 + BK <= p.K) {   // whole step inside K: no per-lane K test
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     dma16(rA, la + j * 1024, a_off[j] + ka);
@@ -344,7 +443,8 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     dma16(rA, la + j * 1024, k0 + 8 * a_c < p.K ? a_off[j] + ka : OOB);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    dma16(rB, lb + j * 1024, k0 + b_k[j] < p.K ? b_off[j] + kb : OOB);
+                    dma16(rB, lb + j * 1024,
+                          k0 + 4 * wave + 2 * j + (lane >> 5) < p.K ? b_off[j] + kb : OOB);
             }
         };
 
@@ -352,12 +452,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // Item (peer pp, row block i) is the wave's 16 x 64 block of that
         // peer partial: rows blk .. blk+15 (blk = m0 + 128*wm + 16*i), columns
         // n0 + 64*wn .. +63.  It moves global -> LDS with two 16-byte DMA
-        // instructions per wave (8 rows of 128 B each); 16-byte chunk c of
-        // block row r is stored at chunk c ^ ((r/2) % 8).  The buffer starts
+        // instructions per wave, stored chunk-major: 16-byte chunk c (columns
+        // 8c .. 8c+7) of block row r sits at (16*c + r) * 16, so lane l of
+        // instruction t fetches row l%16, chunk 4*t + l/16.  The buffer starts
         // at the first row that may be read (>= row_lo) and ends at row_hi,
         // so rows outside [row_lo, row_hi) read as zero (rows below wrap past
         // 2^31); chunks past N are masked per lane on edge tiles.  Items
-        // outside [0, W) load nothing (an empty buffer).
+        // outside [wlo, whi) load nothing (an empty buffer).
         const int pm_base = m0 + wm * WM + fi;
         const int pn_base = n0 + wn * WN + 4 * fg;
         const int row_lo = MODE == MODE_RS ? p.lo : 0;
@@ -365,35 +466,29 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         int W = 0;
         if (PEERS && m0 < row_hi && m0 + BM > row_lo)
             W = p.npeers * FM;
-        uint32_t pd_off[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int row = 8 * r + (lane >> 3);
-            const int c = (lane & 7) ^ ((row >> 1) & 7);
-            const int n = n0 + wn * WN + 8 * c;
-            pd_off[r] = n < p.N ? (uint32_t)row * N2 + (uint32_t)n * 2u : OOB;
-        }
-        auto peer_dma = [&](const uint8_t *slotbuf, int w, int i) {
-            const bool live_item = w >= 0 && w < W;
+        // chunk of instruction 0 is lane/16, of instruction 1 lane/16 + 4
+        const int pd_n = n0 + wn * WN + 8 * (lane >> 4);
+        const uint32_t pd_off = (uint32_t)(lane & 15) * N2 + (uint32_t)pd_n * 2u;
+        // Items this segment adds: those whose step lies in it (the drain
+        // after the K loop moves the window to the items past KT).
+        int wlo = g0, whi = min(g1, W);
+        auto peer_dma = [&](const uint8_t *slotbuf, int w, int i, uint32_t pd_off, int pd_n) {
+            const bool live_item = w >= wlo && w < whi;
             const int pp = live_item ? (w >> 3) : 0;
             const int blk = m0 + wm * WM + 16 * i;
             const int start = max(blk, row_lo);
             const int rows = live_item ? max(row_hi - start, 0) : 0;
             const u32x4_t rp = make_rsrc4(
                 p.partials + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
-            const uint32_t shift = (uint32_t)(start - blk) * N2;
+            const uint32_t off = pd_off - (uint32_t)(start - blk) * N2;
             const uint32_t ls = lds_addr(slotbuf) + (uint32_t)(wave * PSLOT);
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-                dma16(rp, ls + r * 1024, pd_off[r] == OOB ? OOB : pd_off[r] - shift);
+            dma16(rp, ls, pd_n < p.N ? off : OOB);
+            dma16(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
         };
         // Reading back: lane (fi, fg) needs row fi, columns 16*j + 4*fg .. +3,
-        // i.e. half fg%2 of logical chunk 2*j + fg/2.
-        uint32_t pc_off[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            pc_off[j] = (uint32_t)(fi * 128 + (((2 * j + (fg >> 1)) ^ ((fi >> 1) & 7)) << 4) +
-                                   8 * (fg & 1));
+        // i.e. half fg%2 of chunk 2*j + fg/2: byte j*512 + pc_off.  The 32
+        // lanes of one ds_read_b64 pass read 256 contiguous bytes.
+        const uint32_t pc_off = (uint32_t)(((fg >> 1) * 16 + fi) * 16 + 8 * (fg & 1));
 
         f32x4_t acc[FM][FN];
 #pragma unroll
@@ -402,18 +497,21 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-        auto read_frags = [&](const uint8_t *cA, const uint8_t *cB, bf16x8_t (&fa)[FN],
-                              bf16x8_t (&fb)[FM]) {
+        auto read_frags = [&](const uint8_t *cA, bf16x8_t (&fa)[FN], bf16x8_t (&fb)[FM]) {
+            const uint32_t sa = opaque(lds_addr(cA)), sb = sa + A_BYTES;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const uint8_t *base = cB + b_frag_j[j];
-                bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base));
-                bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(base + 4 * 512));
+                const uint32_t base = sb + b_frag_j[j];
+                bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4_t *)lds_ptr<bf16x4_t>(base));
+                bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4_t *)lds_ptr<bf16x4_t>(base + 4 * 512));
                 fa[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
+            const uint32_t ab = sa + a_frag;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                fb[i] = *(const bf16x8_t *)(cA + a_frag + i * 16 * 64);
+                fb[i] = *lds_ptr<bf16x8_t>(ab + i * 16 * 64);
         };
         auto mfmas = [&](const bf16x8_t (&fa)[FN], const bf16x8_t (&fb)[FM]) {
 #pragma unroll
@@ -423,17 +521,19 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
         };
 
-        // Prologue: virtual steps -3, -2, -1 issue stages 0, 1, 2 and peer
-        // items -1 (nothing), 0, 1, exactly as a loop step would.
-        dma_stage(0, sS0, sS0 + A_BYTES);
+        // Prologue: virtual steps g0-3, g0-2, g0-1 issue stages g0 .. g0+2 and
+        // peer items g0-1 (nothing), g0, g0+1, exactly as a loop step would.
+        // (g0 is a multiple of 8: the stage ring restarts at the segment, the
+        // slot of item w is w % 2 and its row block w % 8.)
+        dma_stage(g0, sS0, sS0 + A_BYTES);
         if (PEERS)
-            peer_dma(sP1, -1, 7);
-        dma_stage(1, sS1, sS1 + A_BYTES);
+            peer_dma(sP1, g0 - 1, 7, pd_off, pd_n);
+        dma_stage(g0 + 1, sS1, sS1 + A_BYTES);
         if (PEERS)
-            peer_dma(sP0, 0, 0);
-        dma_stage(2, sS2, sS2 + A_BYTES);
+            peer_dma(sP0, g0, 0, pd_off, pd_n);
+        dma_stage(g0 + 2, sS2, sS2 + A_BYTES);
         if (PEERS)
-            peer_dma(sP1, 1, 1);
+            peer_dma(sP1, g0 + 1, 1, pd_off, pd_n);
 
         // ---- main loop: ping-pong between the two waves of each SIMD ----
         // Waves 0-3 (group 0) and 4-7 (group 1) sit one per SIMD each.  Step
@@ -455,11 +555,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         wait_vmcnt<AFTER>();          // own loads of stage 0 done
         if (lag)
             barrier_only();
-        for (int kt0 = 0; kt0 < KT; kt0 += 8) {
+        for (int kt0 = g0; kt0 < g1; kt0 += 8) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int kt = kt0 + u;
-                if (kt < KT) {
+                if (kt < g1) {
                     uint8_t *cS = (u & 3) == 0 ? sS0 : (u & 3) == 1 ? sS1 : (u & 3) == 2 ? sS2 : sS3;
                     uint8_t *nS = (u & 3) == 0 ? sS3 : (u & 3) == 1 ? sS0 : (u & 3) == 2 ? sS1 : sS2;
                     uint8_t *cA = cS, *cB = cS + A_BYTES, *nA = nS, *nB = nS + A_BYTES;
@@ -467,23 +567,24 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     // ---- M(kt) ----
                     barrier_only();
                     bf16x8_t fa[FN], fb[FM];
-                    read_frags(cA, cB, fa, fb);
+                    read_frags(cA, fa, fb);
                     dma_stage(kt + 3, nA, nB);
                     if (PEERS) {
                         // Item kt was issued in M(kt-2); after it came stage
                         // kt+2, item kt+1 and stage kt+3.
                         wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
-                        if (kt < W) {
+                        if (kt < whi) {
                             u32x2_t pv[FN];
+                            const uint32_t pb = opaque(lds_addr(sl)) + wave * PSLOT;
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
-                                pv[j] = *(const u32x2_t *)(sl + wave * PSLOT + pc_off[j]);
+                                pv[j] = *lds_ptr<u32x2_t>(pb + pc_off + j * 512);
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
                                 acc[u][j] += unpack_bf16x4(pv[j]);
                         }
                         wait_lgkmcnt0();  // slot read back before it is refilled
-                        peer_dma(sl, kt + 2, (u + 2) & 7);
+                        peer_dma(sl, kt + 2, (u + 2) & 7, pd_off, pd_n);
                     }
                     wait_vmcnt<AFTER>();  // own loads of stage kt+1 done
                     wait_lgkmcnt0();      // stage kt fully read into registers
@@ -496,29 +597,110 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         if (!lag)
             barrier_only();           // same barrier count in both groups
 
+        // Lane offsets for the rest of the segment, recomputed (see opaque_v).
+        const int ln = opaque_v(lane);
+        const int fi2 = ln & 15, fg2 = ln >> 4;
+        const int pm_base2 = m0 + wm * WM + fi2;
+        const int pn_base2 = n0 + wn * WN + 4 * fg2;
+
+        // ---- stream-K: hand the partial over, or collect the partials ----
+        // A partial is stored in accumulator order (wave, block, lane), 16
+        // bytes per lane per block, so every access is a full 1 KiB per wave.
+        // (Buffer accesses: one lane offset plus a scalar block offset, so no
+        // 64-bit address is held per block.)
+        const uint32_t part_lane = (uint32_t)((wave * FM * FN * 64 + ln) * 16);
+        auto part_rsrc = [&](int slot) {
+            return make_rsrc(p.sk_part + (size_t)slot * PART_FLOATS, PART_FLOATS * 4u);
+        };
+        if (contrib) {
+            const __amdgpu_buffer_rsrc_t rp = part_rsrc(v);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)part_lane,
+                        (int)((i * FN + j) * 64 * 16), CPOL_SYS);
+            signal_partial(1u);
+            continue;
+        }
+        if (owner) {
+            // The rest of the tile, [g1, KT), was run by the workgroups before
+            // this one in stream-K order (v-1, v-2, ...), sk_iters steps each,
+            // at the start of their runs.  Each wave waits for the flag
+            // itself and reads back only its own part of each partial, so no
+            // barrier or LDS cell is needed.
+            int vv = v - 1;
+            for (int cur = g1; cur < KT; cur += p.sk_iters, --vv) {
+                int ok = 0;
+                if (lane == 0) {
+                    uint32_t spins = 0;
+                    for (;;) {
+                        uint32_t f = __hip_atomic_load(p.sk_flags + 2 * vv, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_SYSTEM);
+                        if ((int32_t)(f - p.sk_epoch) >= 0) {
+                            ok = (int)__hip_atomic_load(p.sk_flags + 2 * vv + 1, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_SYSTEM);
+                            break;
+                        }
+                        if (++spins >= p.sk_max_spins) {
+                            if (p.status)
+                                atomicCAS(p.status, 0, 1000 + 16);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                ok = __builtin_amdgcn_readfirstlane(ok);
+                if (!ok) {             // partner timed out: leave the tile unwritten
+                    g1 = -1;
+                    break;
+                }
+                // one row block at a time: 16 registers in flight, not 128
+                const __amdgpu_buffer_rsrc_t rp = part_rsrc(vv);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] += __builtin_bit_cast(
+                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rp, (int)part_lane, (int)((i * FN + j) * 64 * 16),
+                                         CPOL_SYS));
+                }
+            }
+            if (g1 < 0)
+                continue;
+        }
+
         // ---- peer items the K loop did not reach: two per round trip ----
         if (PEERS && W > KT) {
             wait_vmcnt<0>();
+            wlo = KT;
+            whi = W;
+            const int pd_n2 = n0 + wn * WN + 8 * (ln >> 4);
+            const uint32_t pd_off2 = (uint32_t)(ln & 15) * N2 + (uint32_t)pd_n2 * 2u;
+            const uint32_t pc_off2 = (uint32_t)(((fg2 >> 1) * 16 + fi2) * 16 + 8 * (fg2 & 1));
             for (int w0 = KT & ~7; w0 < W; w0 += 8) {
 #pragma unroll
                 for (int i = 0; i < FM; i += 2) {
                     const bool a = w0 + i >= KT, b = w0 + i + 1 >= KT;
                     if (a)
-                        peer_dma(sP0, w0 + i, i);
+                        peer_dma(sP0, w0 + i, i, pd_off2, pd_n2);
                     if (b)
-                        peer_dma(sP1, w0 + i + 1, i + 1);
+                        peer_dma(sP1, w0 + i + 1, i + 1, pd_off2, pd_n2);
                     wait_vmcnt<0>();
                     if (a) {
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
                             acc[i][j] += unpack_bf16x4(
-                                *(const u32x2_t *)(sP0 + wave * PSLOT + pc_off[j]));
+                                *(const u32x2_t *)(sP0 + wave * PSLOT + pc_off2 + j * 512));
                     }
                     if (b) {
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
                             acc[i + 1][j] += unpack_bf16x4(
-                                *(const u32x2_t *)(sP1 + wave * PSLOT + pc_off[j]));
+                                *(const u32x2_t *)(sP1 + wave * PSLOT + pc_off2 + j * 512));
                     }
                     wait_lgkmcnt0();  // reads done before the slots refill
                 }
@@ -532,13 +714,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const int s0 = p.rank * p.P;   // first global row of the slice
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int m = pm_base + 16 * i;
+                const int m = pm_base2 + 16 * i;
                 const bool in_slice = m >= s0 && m < s0 + p.P;
                 const bool to_ws = !in_slice && m < p.M;
-                const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn_base * 2u;
+                const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn_base2 * 2u;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const bool ok = pn_base + 16 * j < p.N;
+                    const bool ok = pn_base2 + 16 * j < p.N;
                     const u32x2_t v = pack_bf16x4(acc[i][j]);
                     store8(ro, (ok && in_slice) ? rbase + 32u * j : OOB, v);
                     store8(rw, (ok && to_ws) ? rbase + 32u * j : OOB, v);
@@ -549,11 +731,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)p.M * N2);
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int m = pm_base + 16 * i;
-                const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn_base * 2u;
+                const int m = pm_base2 + 16 * i;
+                const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const bool ok = m < p.M && pn_base + 16 * j < p.N;
+                    const bool ok = m < p.M && pn_base2 + 16 * j < p.N;
                     store8(ro, ok ? rbase + 32u * j : OOB, pack_bf16x4(acc[i][j]));
                 }
             }

@@ -13,7 +13,8 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+std::atomic<int> g_cu_count[kMaxDevices];      // 0 = not queried yet
+std::atomic<uint32_t> g_epoch[kMaxDevices];    // stream-K launch counter
 
 int cu_count(int dev)
 {
@@ -60,8 +61,16 @@ int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64
     return GC_OK;
 }
 
+// Workspace layout: two flag words per workgroup (rounded up to 256 bytes),
+// then one fp32 partial tile per workgroup.
+int64_t flags_bytes(int groups) { return ((int64_t)groups * 8 + 255) / 256 * 256; }
+int64_t workspace_bytes_for(int groups)
+{
+    return flags_bytes(groups) + (int64_t)groups * gc::PART_FLOATS * 4;
+}
+
 template <int MODE>
-int dispatch(gc::Args &a, hipStream_t stream)
+int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
@@ -76,10 +85,36 @@ int dispatch(gc::Args &a, hipStream_t stream)
     a.group_m = 4;
     if (a.num_tiles == 0)
         return GC_OK;
-    // One 256-thread workgroup per CU (the kernel holds 128 KiB of LDS);
-    // a persistent workgroup walks its tiles round by round.
+    // One 512-thread workgroup per CU (the kernel holds up to 160 KiB of
+    // LDS); a persistent workgroup walks its list of tiles and segments.
     const int cus = cu_count(dev);
-    const int grid = a.num_tiles < cus ? a.num_tiles : cus;
+    const int kt = (a.K + gc::BK - 1) / gc::BK;
+    const int kt8 = (kt + 7) / 8 * 8;
+    const bool split = peers->workspace && kt > 0 &&
+                       peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus) &&
+                       (int64_t)a.num_tiles * kt8 < INT32_MAX;
+    int grid;
+    if (split) {
+        // Whole tiles while at least two full rounds remain; the last one to
+        // two rounds' worth of tiles is split along K over all workgroups.
+        const int T = a.num_tiles;
+        a.dp_tiles = T >= 2 * cus ? (T / cus - 1) * cus : 0;
+        a.sk_tiles = T - a.dp_tiles;
+        a.kt8 = kt8;
+        const int64_t sk_total = (int64_t)a.sk_tiles * kt8;
+        a.sk_iters = (int)(((sk_total + cus - 1) / cus + 7) / 8 * 8);
+        a.sk_flags = (uint32_t *)peers->workspace;
+        a.sk_part = (float *)((char *)peers->workspace + flags_bytes(cus));
+        a.sk_epoch = g_epoch[dev < kMaxDevices ? dev : 0].fetch_add(1) + 1;
+        a.sk_max_spins = 1u << 22;
+        grid = cus;
+    } else {
+        a.dp_tiles = a.num_tiles;
+        a.sk_tiles = 0;
+        a.kt8 = kt8;
+        a.sk_iters = 0;
+        grid = a.num_tiles < cus ? a.num_tiles : cus;
+    }
     hipLaunchKernelGGL((gc::gc_kernel<MODE>), dim3(grid), dim3(gc::NT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
 }
@@ -89,6 +124,14 @@ int dispatch(gc::Args &a, hipStream_t stream)
 extern "C" {
 
 int gemm_coll_should_run(int64_t M) { return M >= 128 ? 1 : 0; }
+
+int64_t gemm_coll_workspace_bytes(void)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GC_EIO;
+    return workspace_bytes_for(cu_count(dev));
+}
 
 const char *gemm_coll_strerror(int code)
 {
@@ -131,7 +174,8 @@ int gemm_ar(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
     a.rank = rank;
     a.npeers = R - 1;
     a.m_rows = (int)M;
-    return dispatch<gc::MODE_AR>(a, (hipStream_t)stream);
+    a.status = peers->status;
+    return dispatch<gc::MODE_AR>(a, peers, (hipStream_t)stream);
 }
 
 int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
@@ -171,7 +215,8 @@ int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
     a.lo = (int)lo;
     a.hi = (int)hi;
     a.m_rows = (int)(end > M ? end : M);
-    return dispatch<gc::MODE_RS>(a, (hipStream_t)stream);
+    a.status = peers->status;
+    return dispatch<gc::MODE_RS>(a, peers, (hipStream_t)stream);
 }
 
 int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K, int R, int rank,
@@ -202,7 +247,7 @@ int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K
     a.R = R;
     a.rank = rank;
     a.m_rows = (int)Ms;
-    return dispatch<gc::MODE_AG>(a, (hipStream_t)stream);
+    return dispatch<gc::MODE_AG>(a, peers, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -34,7 +34,7 @@ def header_functions():
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"gemm_ar", "gemm_rs", "ag_gemm", "gemm_coll_should_run",
-                          "gemm_coll_strerror"}, names
+                          "gemm_coll_strerror", "gemm_coll_workspace_bytes"}, names
     out = subprocess.run(["nm", "-D", "--defined-only", gc.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -51,7 +51,9 @@ def test_peers_struct_layout(tmp_path):
         "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu\\n\","
         "offsetof(gc_peers,partials),offsetof(gc_peers,ws),offsetof(gc_peers,shards),"
         "offsetof(gc_peers,flags),offsetof(gc_peers,epoch),offsetof(gc_peers,status),"
-        "offsetof(gc_peers,max_spins),sizeof(gc_peers));return 0;}\n")
+        "offsetof(gc_peers,max_spins),sizeof(gc_peers));"
+        "printf(\"%zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes));"
+        "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
                     str(src)], check=True)
@@ -59,7 +61,8 @@ def test_peers_struct_layout(tmp_path):
                                              check=True).stdout.split()]
     P = gc.GcPeers
     py_vals = [P.partials.offset, P.ws.offset, P.shards.offset, P.flags.offset, P.epoch.offset,
-               P.status.offset, P.max_spins.offset, ctypes.sizeof(P)]
+               P.status.offset, P.max_spins.offset, ctypes.sizeof(P), P.workspace.offset,
+               P.workspace_bytes.offset]
     assert c_vals == py_vals
 
 

@@ -1,0 +1,154 @@
+"""Work split along K (stream-K): tiles shared by several workgroups must give
+exactly what whole tiles give on integer inputs (every partial sum exact in
+fp32), in all three modes, across shapes that exercise the split: fewer tiles
+than compute units, a tile shared by many workgroups, K-step counts that are
+not a multiple of the segment granularity, and back-to-back launches (the
+partial-ready flags carry a per-launch epoch and are never reset)."""
+import numpy as np
+import pytest
+import torch
+
+import tensor_bf16_gemm_amd as gc
+import workloads as wl
+from gpu_util import assert_bits_equal, assert_close, host_bits, log
+from oracle.oracle import load as load_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SENTINEL = 0x7FC1
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return load_oracle()
+
+
+def to_dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+def filled(shape):
+    return torch.full(shape, SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+
+
+SHAPES = [
+    (300, 1040, 1024, 8),    # 10 tiles, 32 K-steps: tiles split over 4 workgroups
+    (64, 264, 4096, 4),      # 2 tiles, 128 K-steps: each tile over 16 workgroups
+    (513, 520, 896, 2),      # 28 K-steps (not a multiple of 8)
+    (1000, 776, 72, 8),      # 3 K-steps: every tile fits one workgroup's run
+    (4096, 1552, 512, 8),    # 112 tiles
+    (2304, 2560, 256, 4),    # 90 tiles
+]
+
+
+@pytest.mark.parametrize("M,N,K,R", SHAPES)
+def test_ar_split_equals_whole(orc, M, N, K, R):
+    log(f"stream-K AR M={M} N={N} K={K} R={R}")
+    xc = wl.integer_inputs("ar", M, N, K, R, seed=M + N + K)
+    x = to_dev(xc)
+    whole = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=1, workspace=False)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=1, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert_bits_equal(host_bits(split), host_bits(whole), "split vs whole")
+    assert_bits_equal(host_bits(split), orc.gemm_ar(host_bits(xc["A"]), host_bits(xc["B"]),
+                                                    host_bits(xc["peers"]), R), "split vs oracle")
+
+
+@pytest.mark.parametrize("M,N,K,R", SHAPES[:3])
+def test_rs_split_all_ranks(orc, M, N, K, R):
+    log(f"stream-K RS M={M} N={N} K={K} R={R}")
+    xc = wl.integer_inputs("rs", M, N, K, R, seed=M + 2 * K)
+    x = to_dev(xc)
+    A, B, peers = (host_bits(xc[k]) for k in ("A", "B", "peers"))
+    for rank in range(R):
+        ws = filled((M, N))
+        out = gc.gemm_rs(x["A"], x["B"], x["peers"], ws, R=R, rank=rank)
+        torch.cuda.synchronize()
+        ws_ref = np.full((M, N), SENTINEL, np.uint16)
+        ref, ws_ref = orc.gemm_rs(A, B, peers, R, rank, ws_ref)
+        assert_bits_equal(host_bits(out), ref, f"RS split rank {rank}")
+        assert_bits_equal(host_bits(ws), ws_ref, f"RS split ws rank {rank}")
+
+
+@pytest.mark.parametrize("Ms,N,K,R", [(100, 520, 1024, 4), (512, 1040, 896, 8)])
+def test_ag_split(orc, Ms, N, K, R):
+    log(f"stream-K AG Ms={Ms} N={N} K={K} R={R}")
+    rank = R - 1
+    xc = wl.integer_inputs("ag", Ms, N, K, R, rank=rank, seed=Ms + K)
+    x = to_dev(xc)
+    flags = torch.ones(R, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, R=R, rank=rank, epoch=1)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    sh = host_bits(xc["shards"])
+    assert_bits_equal(host_bits(out), orc.ag_gemm(sh[rank].copy(), host_bits(xc["B"]), sh, R, rank),
+                      "AG split")
+
+
+def test_back_to_back_launches(orc):
+    """Many launches on one workspace: each must see only its own partials."""
+    M, N, K, R = 300, 520, 2048, 4
+    outs = []
+    inputs = []
+    for i in range(6):
+        xc = wl.integer_inputs("ar", M, N, K, R, seed=100 + i)
+        x = to_dev(xc)
+        inputs.append(xc)
+        outs.append(gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=0))
+    torch.cuda.synchronize()
+    for i, (xc, o) in enumerate(zip(inputs, outs)):
+        assert_bits_equal(host_bits(o), orc.gemm_ar(host_bits(xc["A"]), host_bits(xc["B"]),
+                                                    host_bits(xc["peers"]), R), f"launch {i}")
+
+
+def test_split_float_inputs_close(orc):
+    """Float inputs: the split changes only the fp32 summation order."""
+    w = wl.Workload("sk", "ar", 512, 6288, 7168, 8, 0, 1.0, 1 / np.sqrt(7168))
+    x = wl.make_inputs(w, device=DEV)
+    a = gc.gemm_ar(x["A"], x["B"], x["peers"], R=8, rank=0)
+    b = gc.gemm_ar(x["A"], x["B"], x["peers"], R=8, rank=0, workspace=False)
+    torch.cuda.synchronize()
+    assert_close(host_bits(a), host_bits(b), "split vs whole (float)")
+
+
+@pytest.mark.parametrize("mode,M,N,K,R", [
+    ("ar", 4352, 4096, 64, 2),   # 17 x 16 = 272 tiles: one full round of 256, then 16
+    ("rs", 4352, 4104, 40, 4),   # 17 x 17 = 289 tiles, ragged N and K
+    ("ag", 600, 4096, 72, 8),    # 8 shards x 3 x 16 = 384 tiles
+])
+def test_whole_tiles_partial_last_round(orc, mode, M, N, K, R):
+    """Whole tiles only (no workspace) with more tiles than compute units and a
+    last round that leaves workgroups idle: every tile exactly once."""
+    log(f"whole tiles {mode} M={M} N={N} K={K} R={R}")
+    rank = 1
+    xc = wl.integer_inputs(mode, M, N, K, R, rank=rank, seed=M + N)
+    x = to_dev(xc)
+    Bh = host_bits(xc["B"])
+    if mode == "ar":
+        out = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=rank,
+                         workspace=False)
+        torch.cuda.synchronize()
+        ref = orc.gemm_ar(host_bits(xc["A"]), Bh, host_bits(xc["peers"]), R)
+        assert_bits_equal(host_bits(out), ref, "AR whole tiles")
+    elif mode == "rs":
+        ws = filled((M, N))
+        out = gc.gemm_rs(x["A"], x["B"], x["peers"], ws, R=R, rank=rank, workspace=False)
+        torch.cuda.synchronize()
+        ws_ref = np.full((M, N), SENTINEL, np.uint16)
+        ref, ws_ref = orc.gemm_rs(host_bits(xc["A"]), Bh, host_bits(xc["peers"]), R, rank, ws_ref)
+        assert_bits_equal(host_bits(out), ref, "RS whole tiles")
+        assert_bits_equal(host_bits(ws), ws_ref, "RS whole tiles ws")
+    else:
+        flags = torch.ones(R, dtype=torch.int32, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        out = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, filled((R * M, N)), R=R,
+                         rank=rank, epoch=1, workspace=False)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        sh = host_bits(xc["shards"])
+        assert_bits_equal(host_bits(out), orc.ag_gemm(sh[rank].copy(), Bh, sh, R, rank),
+                          "AG whole tiles")
