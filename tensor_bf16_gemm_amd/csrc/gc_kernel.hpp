@@ -340,6 +340,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // done reading its LDS stages before this segment's loads reuse them.
         wait_vmcnt<0>();
         barrier_only();
+        // Fragment offsets, redefined here: if the compiler parked them in
+        // scratch, their reload completes now and not through a wait for
+        // every outstanding load at the top of each pass of the K loop.
+        uint32_t bfj[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bfj[j] = (uint32_t)opaque_v((int)b_frag_j[j]);
+        const uint32_t afr = (uint32_t)opaque_v((int)a_frag);
 
         // Raise this workgroup's partial-ready flag (after its partial, if
         // any, is stored and written back).
@@ -501,14 +509,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const uint32_t sa = opaque(lds_addr(cA)), sb = sa + A_BYTES;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const uint32_t base = sb + b_frag_j[j];
+                const uint32_t base = sb + bfj[j];
                 bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                     (lds_bf16x4_t *)lds_ptr<bf16x4_t>(base));
                 bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                     (lds_bf16x4_t *)lds_ptr<bf16x4_t>(base + 4 * 512));
                 fa[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            const uint32_t ab = sa + a_frag;
+            const uint32_t ab = sa + afr;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
                 fb[i] = *lds_ptr<bf16x8_t>(ab + i * 16 * 64);

@@ -95,10 +95,11 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
                        (int64_t)a.num_tiles * kt8 < INT32_MAX;
     int grid;
     if (split) {
-        // Whole tiles while at least two full rounds remain; the last one to
-        // two rounds' worth of tiles is split along K over all workgroups.
+        // Whole tiles for every full round of workgroups; only the tiles of
+        // the last, partial round are split along K over all workgroups
+        // (splitting more keeps fewer A and B panels shared in L2).
         const int T = a.num_tiles;
-        a.dp_tiles = T >= 2 * cus ? (T / cus - 1) * cus : 0;
+        a.dp_tiles = T / cus * cus;
         a.sk_tiles = T - a.dp_tiles;
         a.kt8 = kt8;
         const int64_t sk_total = (int64_t)a.sk_tiles * kt8;
