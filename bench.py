@@ -95,6 +95,61 @@ def read_traffic(w, kernel_us: float):
     return entry.get("bytes_per_launch")
 
 
+def _counter_means(run_dir: str, counter: str) -> dict:
+    """Mean value of `counter` per kernel name over the dispatches recorded in
+    a rocprofv3 --pmc run directory (its *counter_collection.csv files)."""
+    import csv
+    import glob
+    vals: dict = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def ingest_counters(name: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str,
+                    cal_write_dir: str) -> dict:
+    """HBM bytes per launch of the fused kernel from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of this benchmark, and the
+    same two counters for `--calibrate-copy` (a 1 GiB device copy, so 1 GiB
+    read and 1 GiB written).  Each counter is divided by what it reads for the
+    copy per byte moved.  Writes the entry into profiles/traffic.json."""
+    n = 1 << 30
+
+    def kernel_kib(d, counter):
+        m = _counter_means(d, counter)
+        ks = [k for k in m if "gc_kernel" in k]
+        if len(ks) != 1:
+            raise SystemExit(f"{d}: expected one gc_kernel entry for {counter}, found {ks}")
+        return m[ks[0]]
+
+    def copy_kib(d, counter):
+        m = _counter_means(d, counter)
+        if not m:
+            raise SystemExit(f"{d}: no {counter} records")
+        return max(m.values())          # the 1 GiB copy dominates every other kernel
+
+    f_fetch = copy_kib(cal_fetch_dir, "FETCH_SIZE") * 1024 / n
+    f_write = copy_kib(cal_write_dir, "WRITE_SIZE") * 1024 / n
+    fetch = kernel_kib(fetch_dir, "FETCH_SIZE") * 1024 / f_fetch
+    write = kernel_kib(write_dir, "WRITE_SIZE") * 1024 / f_write
+    entry = {"source_digest": source_digest(), "bytes_per_launch": fetch + write,
+             "fetch_bytes": fetch, "write_bytes": write,
+             "copy_factor_fetch": f_fetch, "copy_factor_write": f_write}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        t = {}
+    t.setdefault("workloads", {})[name] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return entry
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the CPU oracle on leading rows of the workload (about target_s)."""
     import torch
@@ -160,7 +215,16 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc run directories (FETCH_SIZE and WRITE_SIZE of this "
+                         "benchmark, then of --calibrate-copy): write profiles/traffic.json")
     args = ap.parse_args(argv)
+
+    if args.ingest_counters:
+        import workloads as wl
+        name = args.workload or wl.HEADLINE
+        print(json.dumps({name: ingest_counters(name, *args.ingest_counters)}))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
