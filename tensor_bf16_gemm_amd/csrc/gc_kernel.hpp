@@ -172,6 +172,16 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds, uint32_t off)
                  : "memory");
 }
 
+// As dma16, with the system-coherent cache policy (sc0 sc1): the load misses
+// every cache, so it sees data another XCD wrote through to memory.
+__device__ __forceinline__ void dma16_sys(u32x4_t r, uint32_t lds, uint32_t off)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc0 sc1 lds"
+                 :
+                 : "s"(lds), "v"(off), "s"(r)
+                 : "memory");
+}
+
 // 8-byte buffer store.
 __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v)
 {
@@ -635,13 +645,15 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         if (owner) {
             // The rest of the tile, [g1, KT), was run by the workgroups before
             // this one in stream-K order (v-1, v-2, ...), sk_iters steps each,
-            // at the start of their runs.  Each wave waits for the flag
-            // itself and reads back only its own part of each partial, so no
-            // barrier or LDS cell is needed.
-            int vv = v - 1;
-            for (int cur = g1; cur < KT; cur += p.sk_iters, --vv) {
-                int ok = 0;
-                if (lane == 0) {
+            // at the start of their runs.  Lane 0 of each wave waits for all
+            // their flags; then each wave streams its own 32 KiB of every
+            // partial through 16 KiB of the (now idle) LDS stages, in
+            // quarters of 8 KiB kept two in flight, and adds them.
+            const int nparts = (KT - g1 + p.sk_iters - 1) / p.sk_iters;
+            int ok = 1;
+            if (lane == 0) {
+                for (int c = 0; c < nparts && ok; ++c) {
+                    const int vv = v - 1 - c;
                     uint32_t spins = 0;
                     for (;;) {
                         uint32_t f = __hip_atomic_load(p.sk_flags + 2 * vv, __ATOMIC_RELAXED,
@@ -654,31 +666,64 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                         if (++spins >= p.sk_max_spins) {
                             if (p.status)
                                 atomicCAS(p.status, 0, 1000 + 16);
+                            ok = 0;
                             break;
                         }
                         __builtin_amdgcn_s_sleep(2);
                     }
                 }
-                ok = __builtin_amdgcn_readfirstlane(ok);
-                if (!ok) {             // partner timed out: leave the tile unwritten
-                    g1 = -1;
-                    break;
-                }
-                // one row block at a time: 16 registers in flight, not 128
-                const __amdgpu_buffer_rsrc_t rp = part_rsrc(vv);
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] += __builtin_bit_cast(
-                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rp, (int)part_lane, (int)((i * FN + j) * 64 * 16),
-                                         CPOL_SYS));
-                }
             }
-            if (g1 < 0)
-                continue;
+            ok = __builtin_amdgcn_readfirstlane(ok);
+            // Every wave's stage loads (also the out-of-range ones past the
+            // segment, which still write LDS) have landed, and its stage
+            // reads are done, before the stages are reused.  All waves meet
+            // here, also one whose partner timed out.
+            wait_vmcnt<0>();
+            barrier_only();
+            if (!ok)
+                continue;              // a partner timed out: leave the tile unwritten
+            const uint8_t *wst = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1
+                               : (wave >> 1) == 2 ? sS2 : sS3;
+            const uint32_t half0 = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
+            const u32x4_t none = make_rsrc4(p.sk_part, 0u);
+            auto prt = [&](int c) {
+                return c < nparts ? make_rsrc4(p.sk_part + (size_t)(v - 1 - c) * PART_FLOATS,
+                                               PART_FLOATS * 4u)
+                                  : none;
+            };
+            // quarter q of a partial: blocks 8q .. 8q+7 (row blocks 2q, 2q+1)
+            auto load_q = [&](u32x4_t r, int q, uint32_t dst) {
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    dma16_sys(r, dst + (uint32_t)(b * 1024),
+                              (uint32_t)(wave * FM * FN * 64 * 16 + (8 * q + b) * 1024) +
+                                  (uint32_t)lane * 16u);
+            };
+            u32x4_t rc = prt(0);
+            load_q(rc, 0, half0);
+            load_q(rc, 1, half0 + 8192);
+            for (int c = 0; c < nparts; ++c) {
+                const u32x4_t rn = prt(c + 1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t h = half0 + (uint32_t)((q & 1) * 8192);
+                    wait_vmcnt<8>();           // this quarter landed
+                    u32x4_t bl[8];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        bl[b] = *lds_ptr<u32x4_t>(h + (uint32_t)(b * 1024 + lane * 16));
+                    wait_lgkmcnt0();
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        acc[2 * q + (b >> 2)][b & 3] += __builtin_bit_cast(f32x4_t, bl[b]);
+                    // refill this half with the quarter two ahead
+                    if (q < 2)
+                        load_q(rc, q + 2, h);
+                    else
+                        load_q(rn, q - 2, h);
+                }
+                rc = rn;
+            }
         }
 
         // ---- peer items the K loop did not reach: two per round trip ----
