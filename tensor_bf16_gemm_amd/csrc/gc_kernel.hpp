@@ -19,8 +19,11 @@
 //
 // Operand staging:
 //   A stage  [256 m][32 k]  64 B per row; 16-byte chunk c of row m is stored
-//            at chunk c ^ ((m/4) % 4), so the 16 lanes of a ds_read_b128
-//            pass cover all 64 banks.
+//            at chunk c ^ ((m/2) % 4).  A fragment read (lane: row m =
+//            lane%16, chunk lane/16) is then free of bank conflicts on
+//            gfx950; the key (m/4) % 4, conflict-free if a ds_read_b128
+//            served 16 consecutive lanes per pass, measured two-way
+//            conflicts (8 LDS cycles per read instead of 4).
 //   B stage  [32 k][256 n]  512 B per row (B is N-contiguous and stays so);
 //            32-byte chunk q of row k is stored at q ^ f(k) with
 //            f(k) = (k % 4) + 4 * ((k / 8) % 2), so the 32 lanes of a
@@ -276,15 +279,15 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
     // ---- per-lane constants -------------------------------------------------
     // A loader: wave instruction j (0..1) fills LDS rows 16*(2*wave+j) +
     // lane/4 (64 B each); the lane's stored chunk lane%4 holds logical chunk
-    // (lane%4) ^ ((row/4)%4) = (lane%4) ^ (lane/16).
-    const int a_c = (lane & 3) ^ (lane >> 4);
+    // (lane%4) ^ ((row/2)%4) = (lane%4) ^ ((lane/8)%4).
+    const int a_c = (lane & 3) ^ ((lane >> 3) & 3);
     // B loader: wave instruction j (0..1) fills LDS rows k = 4*wave + 2*j +
     // lane/32 (512 B each); the lane's stored 16-byte slot lane%32 is half
     // lane%2 of stored 32-byte chunk (lane%32)/2 = logical chunk ^ f(k).
     const int b_slot = lane & 31;
     // fragment reads
     const int fi = lane & 15, fg = lane >> 4;
-    const uint32_t a_frag = (uint32_t)(wm * WM * 64 + fi * 64 + ((fg ^ (fi >> 2)) << 4));
+    const uint32_t a_frag = (uint32_t)(wm * WM * 64 + fi * 64 + ((fg ^ ((fi >> 1) & 3)) << 4));
     const int fB = (fi >> 2) | ((fg & 1) << 2);
     // B^T block j of this wave is logical 32-byte chunk q = 4*wn + j.
     uint32_t b_frag_j[FN];
