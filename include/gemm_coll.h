@@ -47,10 +47,11 @@
  *                 or more, or a size above INT32_MAX)
  *     GC_EIO      the HIP launch failed
  *   M == 0 (or N == 0) is valid and launches nothing.
- * - Stream-K time-out: if a workgroup waiting for a partner's partial sum
- *   gives up (the partner never ran -- only possible if the device could not
- *   hold all workgroups at once), the tile is left unwritten and, when
- *   peers->status is not NULL, *status is set to GC_TIMEOUT_BASE + 16.
+ * - K-split hand-over: the last workgroup to finish a split tile waits only
+ *   for partners that have already finished their part of the K loop, so no
+ *   call can deadlock.  If that wait still gives up (bounded), the tile is
+ *   left unwritten and, when peers->status is not NULL, *status is set to
+ *   GC_TIMEOUT_BASE + 16.
  */
 #ifndef GEMM_COLL_H
 #define GEMM_COLL_H
@@ -94,12 +95,13 @@ typedef struct gc_peers {
        (about one second). */
     uint32_t max_spins;
     /* All calls, optional: device workspace of at least
-       gemm_coll_workspace_bytes() bytes, zero-filled before its first use
-       and not used by two calls at the same time.  With it, tiles left over
-       after the last full round of workgroups are split along K across all
-       compute units (partial sums exchanged through it); with NULL, every
-       tile is computed whole.  Results agree to rounding of the fp32
-       partial sums. */
+       gemm_coll_workspace_bytes() bytes (about 128 MiB on MI355X),
+       zero-filled before its first use and not used by two calls at the
+       same time.  With it, a problem with fewer 256 x 256 output tiles than
+       compute units has its tiles split along K into chunks run by
+       different workgroups (fp32 partial sums exchanged through it); with
+       NULL, or with a full round of tiles or more, every tile is computed
+       whole.  Results agree to rounding of the fp32 partial sums. */
     void *workspace;
     uint64_t workspace_bytes;
 } gc_peers;

@@ -85,17 +85,23 @@ struct Args {
     int tiles_m, tiles_n;      // per shard for AG
     int num_tiles;             // total (AG: R * tiles_m * tiles_n)
     int group_m;               // row tiles per L2 group
-    // Work split.  The first dp_tiles tiles are taken whole, round by round;
-    // the remaining sk_tiles are split along K ("stream-K"): their K-steps
-    // (kt8 per tile, the step count rounded up to a multiple of 8) are cut
-    // into consecutive runs of sk_iters steps, one run per workgroup.  A tile
-    // shared by several workgroups is finished by the one holding its first
-    // step (the owner); the others leave fp32 partials in sk_part and raise
-    // sk_flags[v] to sk_epoch.
+    // Work split.  The first dp_tiles tiles are taken whole, round by round.
+    // Each of the remaining sk_tiles is cut along K into sk_q chunks of
+    // sk_chunk steps (a multiple of 8; the last may be shorter), giving
+    // sk_units = sk_q * sk_tiles units numbered chunk-major (unit u is chunk
+    // u / sk_tiles of tile u % sk_tiles), dealt round-robin to the
+    // workgroups: the workgroups of one round run the same K range of
+    // neighbouring tiles, so they keep sharing A and B in L2.  A unit that
+    // finishes counts itself in sk_count[tile]; the last of a tile's units
+    // adds the others' fp32 partials and writes the tile, the others leave
+    // their partial in sk_part[u] and raise sk_flags[u].  Nobody waits for a
+    // unit that has not yet counted itself in, so the scheme cannot
+    // deadlock whatever the order in which workgroups get a CU.
     int dp_tiles;
-    int sk_tiles, kt8, sk_iters;
-    uint32_t *sk_flags;        // [gridDim.x]
-    float *sk_part;            // [gridDim.x][BM*BN]
+    int sk_tiles, sk_q, sk_chunk, sk_units;
+    unsigned long long *sk_count;  // [sk_tiles]: (epoch << 32) | arrivals
+    uint32_t *sk_flags;        // [2 * sk_units]: epoch, partial valid
+    float *sk_part;            // [sk_units][BM*BN]
     uint32_t sk_epoch;
     uint32_t sk_max_spins;
 };
@@ -296,18 +302,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         b_frag_j[j] = (uint32_t)((8 * fg + (fi >> 2)) * 512 + (wn >> 1) * 256 + 8 * (fi & 3) +
                                  (((4 * (wn & 1) + j) ^ fB) * 32));
 
-    // Work list of this workgroup: whole tiles round by round, then its run
-    // of stream-K steps, cut at tile boundaries into segments [g0, g1).
-    const int v = xcd_remap(blockIdx.x, G);    // position in stream-K order
+    // Work list of this workgroup: whole tiles round by round, then its
+    // split units u = v, v + G, ..., each the K-steps [g0, g1) of one tile.
+    const int v = xcd_remap(blockIdx.x, G);    // position within a round
     int dp_lin = 0;                            // first tile of the next whole-tile round
-    const int sk_total = p.sk_tiles * p.kt8;
-    // Runs are laid out from the end of the stream-K steps: workgroup v
-    // takes [S - (v+1)*sk_iters, S - v*sk_iters), so a tile's first steps
-    // belong to the higher v (its owner), which waits only for lower v.
-    int it = max(sk_total - (v + 1) * p.sk_iters, 0);
-    const int it_end = max(sk_total - v * p.sk_iters, 0);
+    int unit = v;                              // next split unit of this workgroup
     for (;;) {
         int L, g0, g1;
+        bool bad = false;
         if (dp_lin < p.dp_tiles) {
             const int lin = dp_lin;
             const int live = min(G, p.dp_tiles - lin);
@@ -317,20 +319,15 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             L = lin + xcd_remap(blockIdx.x, live);
             g0 = 0;
             g1 = KT;
-        } else if (it < it_end) {
-            const int tt = it / p.kt8;
-            g0 = it - tt * p.kt8;
-            const int seg_end = min(it_end, (tt + 1) * p.kt8);
-            g1 = min(KT, g0 + (seg_end - it));
-            it = seg_end;
-            L = p.dp_tiles + tt;
-            if (g0 >= KT)
-                continue;                      // only padding steps of the tile
+        } else if (unit < p.sk_units) {
+            const int c = unit / p.sk_tiles;
+            g0 = c * p.sk_chunk;
+            g1 = min(KT, g0 + p.sk_chunk);
+            L = p.dp_tiles + (unit - c * p.sk_tiles);
+            unit += G;
         } else {
             break;
         }
-        const bool contrib = g0 > 0;           // partial for an owner elsewhere
-        const bool owner = g0 == 0 && g1 < KT; // collects partials after its run
 
         // Tile: shard step s (AG), row tile mt, column tile nt, grouped
         // column-major over `group_m` row tiles for L2 reuse.
@@ -362,24 +359,61 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             bfj[j] = (uint32_t)opaque_v((int)b_frag_j[j]);
         const uint32_t afr = (uint32_t)opaque_v((int)a_frag);
 
-        // Raise this workgroup's partial-ready flag (after its partial, if
+        // The split unit being run (derived from the loop state instead of
+        // being kept live across the K loop): whole tiles come first, so
+        // `unit` has moved past v exactly when a unit is running.
+        const bool split = unit != v && p.sk_q > 1;
+        auto cur_unit = [&]() { return unit - G; };
+        auto cur_tile = [&]() { return (unit - G) % p.sk_tiles; };
+        // Count this unit in for its tile; returns (to every thread) how
+        // many of the tile's units, this one included, have arrived in this
+        // launch.  The counter holds the launch epoch in its upper half, so
+        // it never needs resetting.  The count is passed on through the
+        // first word of stage 0, once every load into the stages has landed
+        // and every read of them is done.
+        auto arrive = [&]() {
+            int *cell = (int *)sS0;
+            wait_vmcnt<0>();
+            barrier_only();
+            if (tid == 0) {
+                unsigned long long *ctr = p.sk_count + cur_tile();
+                unsigned long long cur =
+                    __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                unsigned long long nxt;
+                for (;;) {
+                    nxt = (uint32_t)(cur >> 32) == p.sk_epoch
+                              ? cur + 1
+                              : ((unsigned long long)p.sk_epoch << 32) | 1ull;
+                    if (__hip_atomic_compare_exchange_strong(ctr, &cur, nxt, __ATOMIC_RELAXED,
+                                                             __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_SYSTEM))
+                        break;
+                }
+                *cell = (int)(uint32_t)nxt;
+            }
+            __syncthreads();
+            const int n = *cell;
+            __syncthreads();
+            return n;
+        };
+        // Raise the partial-ready flag of unit u (after its partial, if
         // any, is stored and written back).
-        // Flags are two words per workgroup: [2v] the epoch of its last
-        // hand-over, [2v+1] whether that partial is valid.  Partials and
-        // flags move with system-coherent accesses (sc0 sc1: stores write
-        // through, loads miss the L2), so handing one over needs no L2
-        // write-back or invalidation, which would evict the A and B tiles
-        // every other workgroup of the XCD is using.  Order: every store of
-        // the partial completed (vmcnt 0 in every wave), then the valid word,
-        // then the epoch word.
+        // Flags are two words per unit: [2u] the epoch of its last hand-over,
+        // [2u+1] whether that partial is valid.  Partials and flags move with
+        // system-coherent accesses (sc0 sc1: stores write through, loads
+        // miss the L2), so handing one over needs no L2 write-back or
+        // invalidation, which would evict the A and B tiles every other
+        // workgroup of the XCD is using.  Order: every store of the partial
+        // completed (vmcnt 0 in every wave), then the valid word, then the
+        // epoch word.
         auto signal_partial = [&](uint32_t ok) {
             wait_vmcnt<0>();
             barrier_only();
             if (tid == 0) {
-                __hip_atomic_store(p.sk_flags + 2 * v + 1, ok, __ATOMIC_RELAXED,
+                __hip_atomic_store(p.sk_flags + 2 * cur_unit() + 1, ok, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
                 wait_vmcnt<0>();
-                __hip_atomic_store(p.sk_flags + 2 * v, p.sk_epoch, __ATOMIC_RELAXED,
+                __hip_atomic_store(p.sk_flags + 2 * cur_unit(), p.sk_epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
             }
         };
@@ -414,9 +448,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 const int ok = s_ready;
                 __syncthreads();
                 if (!ok) {
-                    if (contrib)
-                        signal_partial(0u);  // the owner must not wait forever
-                    continue;
+                    // The tile cannot be finished.  A split unit still goes
+                    // through the hand-over (with no K-steps and an invalid
+                    // partial) so that the tile's last unit does not wait
+                    // forever.
+                    if (!split)
+                        continue;
+                    bad = true;
+                    g1 = g0;
                 }
             }
         }
@@ -633,30 +672,39 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         auto part_rsrc = [&](int slot) {
             return make_rsrc(p.sk_part + (size_t)slot * PART_FLOATS, PART_FLOATS * 4u);
         };
-        if (contrib) {
-            const __amdgpu_buffer_rsrc_t rp = part_rsrc(v);
+        if (split && arrive() < p.sk_q) {
+            // Not the last of the tile's units: hand the partial over.
+            if (!bad) {
+                const __amdgpu_buffer_rsrc_t rp = part_rsrc(cur_unit());
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)part_lane,
-                        (int)((i * FN + j) * 64 * 16), CPOL_SYS);
-            signal_partial(1u);
+                    for (int j = 0; j < FN; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)part_lane,
+                            (int)((i * FN + j) * 64 * 16), CPOL_SYS);
+            }
+            signal_partial(bad ? 0u : 1u);
             continue;
         }
-        if (owner) {
-            // The rest of the tile, [g1, KT), was run by the workgroups before
-            // this one in stream-K order (v-1, v-2, ...), sk_iters steps each,
-            // at the start of their runs.  Lane 0 of each wave waits for all
-            // their flags; then each wave streams its own 32 KiB of every
-            // partial through 16 KiB of the (now idle) LDS stages, in
-            // quarters of 8 KiB kept two in flight, and adds them.
-            const int nparts = (KT - g1 + p.sk_iters - 1) / p.sk_iters;
+        if (bad)
+            continue;                  // the last unit, but its own chunk is missing
+        if (split) {
+            // The last unit of the tile: every other unit has counted itself
+            // in, so its partial is stored or about to be.  Lane 0 of each
+            // wave waits for their flags; then each wave streams its own
+            // 32 KiB of every partial through 16 KiB of the (now idle) LDS
+            // stages, in quarters of 8 KiB kept two in flight, and adds them.
+            // (uniform; integer division is done in vector registers, and
+            // the buffer descriptors built from these must be scalar)
+            const int mine = __builtin_amdgcn_readfirstlane(cur_unit() / p.sk_tiles);
+            const int tt = __builtin_amdgcn_readfirstlane(cur_tile());
+            const int nparts = p.sk_q - 1;
+            auto slot = [&](int c) { return (c < mine ? c : c + 1) * p.sk_tiles + tt; };
             int ok = 1;
             if (lane == 0) {
                 for (int c = 0; c < nparts && ok; ++c) {
-                    const int vv = v - 1 - c;
+                    const int vv = slot(c);
                     uint32_t spins = 0;
                     for (;;) {
                         uint32_t f = __hip_atomic_load(p.sk_flags + 2 * vv, __ATOMIC_RELAXED,
@@ -680,17 +728,17 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             // Every wave's stage loads (also the out-of-range ones past the
             // segment, which still write LDS) have landed, and its stage
             // reads are done, before the stages are reused.  All waves meet
-            // here, also one whose partner timed out.
+            // here, also one whose partner failed.
             wait_vmcnt<0>();
             barrier_only();
             if (!ok)
-                continue;              // a partner timed out: leave the tile unwritten
+                continue;              // a partner failed: leave the tile unwritten
             const uint8_t *wst = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1
                                : (wave >> 1) == 2 ? sS2 : sS3;
             const uint32_t half0 = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
             const u32x4_t none = make_rsrc4(p.sk_part, 0u);
             auto prt = [&](int c) {
-                return c < nparts ? make_rsrc4(p.sk_part + (size_t)(v - 1 - c) * PART_FLOATS,
+                return c < nparts ? make_rsrc4(p.sk_part + (size_t)slot(c) * PART_FLOATS,
                                                PART_FLOATS * 4u)
                                   : none;
             };

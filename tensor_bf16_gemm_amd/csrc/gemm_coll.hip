@@ -61,12 +61,43 @@ int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64
     return GC_OK;
 }
 
-// Workspace layout: two flag words per workgroup (rounded up to 256 bytes),
-// then one fp32 partial tile per workgroup.
-int64_t flags_bytes(int groups) { return ((int64_t)groups * 8 + 255) / 256 * 256; }
+// Workspace layout for G workgroups: one 8-byte arrival counter per split
+// tile (fewer than G of them), two flag words per split unit, then one fp32
+// partial tile per split unit; at most 2 G units.  Each part starts on a
+// 256-byte boundary.
+constexpr int kMaxUnitsPerGroup = 2;
+int64_t a256(int64_t x) { return (x + 255) / 256 * 256; }
+int64_t count_bytes(int groups) { return a256((int64_t)groups * 8); }
+int64_t flag_bytes(int groups) { return a256((int64_t)groups * kMaxUnitsPerGroup * 8); }
 int64_t workspace_bytes_for(int groups)
 {
-    return flags_bytes(groups) + (int64_t)groups * gc::PART_FLOATS * 4;
+    return count_bytes(groups) + flag_bytes(groups) +
+           (int64_t)groups * kMaxUnitsPerGroup * gc::PART_FLOATS * 4;
+}
+
+// Chunk size for the sk_tiles tiles left after the full rounds (sk_tiles <
+// groups), from a cost model in K-step units: the units run in
+// ceil(q * sk_tiles / groups) rounds of `chunk` steps plus a fixed cost per
+// unit (pipeline fill and drain, the partial hand-over), and the last unit
+// of each tile reads q - 1 partials.  Returns `kt` (no split) when splitting
+// does not pay.
+int pick_chunk(int kt, int sk_tiles, int groups)
+{
+    constexpr int kFill = 4, kHandOver = 4, kPartial = 8;
+    int best = kt, best_cost = kt + kFill;
+    for (int chunk = 8; chunk < kt; chunk += 8) {
+        const int q = (kt + chunk - 1) / chunk;
+        const int64_t units = (int64_t)q * sk_tiles;
+        if (units > (int64_t)kMaxUnitsPerGroup * groups)
+            continue;
+        const int rounds = (int)((units + groups - 1) / groups);
+        const int cost = rounds * (chunk + kFill + kHandOver) + kPartial * (q - 1);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = chunk;
+        }
+    }
+    return best;
 }
 
 template <int MODE>
@@ -89,32 +120,34 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     // LDS); a persistent workgroup walks its list of tiles and segments.
     const int cus = cu_count(dev);
     const int kt = (a.K + gc::BK - 1) / gc::BK;
-    const int kt8 = (kt + 7) / 8 * 8;
-    const bool split = peers->workspace && kt > 0 &&
-                       peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus) &&
-                       (int64_t)a.num_tiles * kt8 < INT32_MAX;
-    int grid;
-    if (split) {
-        // Whole tiles for every full round of workgroups; only the tiles of
-        // the last, partial round are split along K over all workgroups
-        // (splitting more keeps fewer A and B panels shared in L2).
-        const int T = a.num_tiles;
-        a.dp_tiles = T / cus * cus;
-        a.sk_tiles = T - a.dp_tiles;
-        a.kt8 = kt8;
-        const int64_t sk_total = (int64_t)a.sk_tiles * kt8;
-        a.sk_iters = (int)(((sk_total + cus - 1) / cus + 7) / 8 * 8);
-        a.sk_flags = (uint32_t *)peers->workspace;
-        a.sk_part = (float *)((char *)peers->workspace + flags_bytes(cus));
-        a.sk_epoch = g_epoch[dev < kMaxDevices ? dev : 0].fetch_add(1) + 1;
-        a.sk_max_spins = 1u << 22;
-        grid = cus;
-    } else {
-        a.dp_tiles = a.num_tiles;
-        a.sk_tiles = 0;
-        a.kt8 = kt8;
-        a.sk_iters = 0;
-        grid = a.num_tiles < cus ? a.num_tiles : cus;
+    a.dp_tiles = a.num_tiles;
+    a.sk_tiles = a.sk_q = a.sk_chunk = a.sk_units = 0;
+    int grid = a.num_tiles < cus ? a.num_tiles : cus;
+    // Only problems with fewer tiles than workgroups are split along K:
+    // measured at M=4096 (400 tiles on 256 CUs), splitting the tiles of the
+    // last partial round, in any chunk size, was slower than running them
+    // whole.
+    const int rest = a.num_tiles;
+    if (peers->workspace && kt > 8 && a.num_tiles < cus &&
+        peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus)) {
+        // The tiles are split along K into units that run chunk by chunk, so
+        // that concurrent units share A and B in L2.
+        const int chunk = pick_chunk(kt, rest, cus);
+        const int64_t units = (int64_t)((kt + chunk - 1) / chunk) * rest;
+        if (chunk < kt && units <= (int64_t)kMaxUnitsPerGroup * cus) {
+            char *ws = (char *)peers->workspace;
+            a.dp_tiles = a.num_tiles - rest;
+            a.sk_tiles = rest;
+            a.sk_chunk = chunk;
+            a.sk_q = (kt + chunk - 1) / chunk;
+            a.sk_units = a.sk_q * rest;
+            a.sk_count = (unsigned long long *)ws;
+            a.sk_flags = (uint32_t *)(ws + count_bytes(cus));
+            a.sk_part = (float *)(ws + count_bytes(cus) + flag_bytes(cus));
+            a.sk_epoch = g_epoch[dev < kMaxDevices ? dev : 0].fetch_add(1) + 1;
+            a.sk_max_spins = 1u << 22;
+            grid = cus;
+        }
     }
     hipLaunchKernelGGL((gc::gc_kernel<MODE>), dim3(grid), dim3(gc::NT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
