@@ -532,7 +532,8 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // Items this segment adds: those whose step lies in it (the drain
         // after the K loop moves the window to the items past KT).
         int wlo = g0, whi = min(g1, W);
-        auto peer_dma = [&](const uint8_t *slotbuf, int w, int i, uint32_t pd_off, int pd_n) {
+        // Item w into the 2 KiB of LDS at ls.
+        auto peer_dma_at = [&](uint32_t ls, int w, int i, uint32_t pd_off, int pd_n) {
             const bool live_item = w >= wlo && w < whi;
             const int pp = live_item ? (w >> 3) : 0;
             const int blk = m0 + wm * WM + 16 * i;
@@ -541,9 +542,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const u32x4_t rp = make_rsrc4(
                 p.partials + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
             const uint32_t off = pd_off - (uint32_t)(start - blk) * N2;
-            const uint32_t ls = lds_addr(slotbuf) + (uint32_t)(wave * PSLOT);
             dma16(rp, ls, pd_n < p.N ? off : OOB);
             dma16(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
+        };
+        auto peer_dma = [&](const uint8_t *slotbuf, int w, int i, uint32_t pd_off, int pd_n) {
+            peer_dma_at(lds_addr(slotbuf) + (uint32_t)(wave * PSLOT), w, i, pd_off, pd_n);
         };
         // Reading back: lane (fi, fg) needs row fi, columns 16*j + 4*fg .. +3,
         // i.e. half fg%2 of chunk 2*j + fg/2: byte j*512 + pc_off.  The 32
@@ -777,37 +780,43 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             }
         }
 
-        // ---- peer items the K loop did not reach: two per round trip ----
+        // ---- peer items the K loop did not reach: eight per round trip ----
+        // (K shorter than the 8 * npeers item steps.)  The K loop is over, so
+        // each wave stages the up to 8 items of a row-block group in its
+        // 16 KiB of the idle LDS stages, once every wave's stage loads have
+        // landed and its stage reads are done.
         if (PEERS && W > KT) {
             wait_vmcnt<0>();
+            barrier_only();
             wlo = KT;
             whi = W;
             const int pd_n2 = n0 + wn * WN + 8 * (ln >> 4);
             const uint32_t pd_off2 = (uint32_t)(ln & 15) * N2 + (uint32_t)pd_n2 * 2u;
             const uint32_t pc_off2 = (uint32_t)(((fg2 >> 1) * 16 + fi2) * 16 + 8 * (fg2 & 1));
+            const uint8_t *wst = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1
+                               : (wave >> 1) == 2 ? sS2 : sS3;
+            const uint32_t reg = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
             for (int w0 = KT & ~7; w0 < W; w0 += 8) {
 #pragma unroll
-                for (int i = 0; i < FM; i += 2) {
-                    const bool a = w0 + i >= KT, b = w0 + i + 1 >= KT;
-                    if (a)
-                        peer_dma(sP0, w0 + i, i, pd_off2, pd_n2);
-                    if (b)
-                        peer_dma(sP1, w0 + i + 1, i + 1, pd_off2, pd_n2);
-                    wait_vmcnt<0>();
-                    if (a) {
+                for (int i = 0; i < FM; ++i)
+                    if (w0 + i >= KT)
+                        peer_dma_at(reg + (uint32_t)(i * PSLOT), w0 + i, i, pd_off2, pd_n2);
+                wait_vmcnt<0>();
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (w0 + i >= KT) {
+                        u32x2_t pv[FN];
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
-                            acc[i][j] += unpack_bf16x4(
-                                *(const u32x2_t *)(sP0 + wave * PSLOT + pc_off2 + j * 512));
-                    }
-                    if (b) {
+                            pv[j] = *lds_ptr<u32x2_t>(reg + (uint32_t)(i * PSLOT) + pc_off2 +
+                                                      (uint32_t)(j * 512));
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
-                            acc[i + 1][j] += unpack_bf16x4(
-                                *(const u32x2_t *)(sP1 + wave * PSLOT + pc_off2 + j * 512));
+                            acc[i][j] += unpack_bf16x4(pv[j]);
                     }
-                    wait_lgkmcnt0();  // reads done before the slots refill
                 }
+                wait_lgkmcnt0();      // reads done before the region refills
             }
         }
 
