@@ -831,12 +831,19 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 const bool in_slice = m >= s0 && m < s0 + p.P;
                 const bool to_ws = !in_slice && m < p.M;
                 const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn_base2 * 2u;
+                // The 16 rows of the block (uniform): all in the slice, all
+                // outside it, or straddling its edge (both stores, masked).
+                const int blk = m0 + wm * WM + 16 * i;
+                const bool any_out = blk < s0 || blk + 16 > s0 + p.P;
+                const bool any_in = blk + 16 > s0 && blk < s0 + p.P;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const bool ok = pn_base2 + 16 * j < p.N;
                     const u32x2_t v = pack_bf16x4(acc[i][j]);
-                    store8(ro, (ok && in_slice) ? rbase + 32u * j : OOB, v);
-                    store8(rw, (ok && to_ws) ? rbase + 32u * j : OOB, v);
+                    if (any_in)
+                        store8(ro, (ok && in_slice) ? rbase + 32u * j : OOB, v);
+                    if (any_out)
+                        store8(rw, (ok && to_ws) ? rbase + 32u * j : OOB, v);
                 }
             }
         } else {
