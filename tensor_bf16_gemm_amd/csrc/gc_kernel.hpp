@@ -43,11 +43,12 @@
 // n = 4*(l/16) .. +3 -- four consecutive outputs, 8 bytes in memory.
 //
 // Peer partials (AR, RS): the R-1 peer tiles are added into the fp32
-// accumulators while the K loop runs.  Item w = (peer w/8, row block w%8)
-// is the wave's 16 x 64 block of that peer; it is loaded into one of two
-// LDS slots of the wave at step w-2 and added at step w, so the peer traffic
-// streams behind the MFMA work; items the K loop does not reach are added
-// after it.
+// accumulators while the K loop runs.  Item w = (peer w/8 - phase, row
+// block w%8) is the wave's 16 x 64 block of that peer; it is loaded into one
+// of two LDS slots of the wave at step w-2 and added at step w, so the peer
+// traffic streams behind the MFMA work.  The items of a tile take the 8 *
+// peers steps from step 8 * phase on (phase 0 but for tiles split into many
+// K chunks); items the K loop does not reach are added after it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -80,6 +81,10 @@ struct Args {
     int N, K;
     int R, rank;
     int npeers;                // AR/RS: R-1
+    // Peer items of a tile start at step 8 * phase: phase 0 for a whole
+    // tile, tile % peer_phases for a split one (all its units agree).  The
+    // host keeps 8 * (peer_phases - 1 + npeers) <= KT.
+    int peer_phases;
     int P, lo, hi;             // RS: slice height and owned valid rows [lo, hi)
     int m_rows;                // rows covered by tiles (per shard for AG)
     int tiles_m, tiles_n;      // per shard for AG
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
     int dp_lin = 0;                            // first tile of the next whole-tile round
     int unit = v;                              // next split unit of this workgroup
     for (;;) {
-        int L, g0, g1;
+        int L, g0, g1, phase;
         bool bad = false;
         if (dp_lin < p.dp_tiles) {
             const int lin = dp_lin;
@@ -319,11 +324,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             L = lin + xcd_remap(blockIdx.x, live);
             g0 = 0;
             g1 = KT;
+            phase = 0;
         } else if (unit < p.sk_units) {
             const int c = unit / p.sk_tiles;
             g0 = c * p.sk_chunk;
             g1 = min(KT, g0 + p.sk_chunk);
             L = p.dp_tiles + (unit - c * p.sk_tiles);
+            phase = __builtin_amdgcn_readfirstlane(p.peer_phases > 1 ? L % p.peer_phases : 0);
             unit += G;
         } else {
             break;
@@ -530,17 +537,20 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int pd_n = n0 + wn * WN + 8 * (lane >> 4);
         const uint32_t pd_off = (uint32_t)(lane & 15) * N2 + (uint32_t)pd_n * 2u;
         // Items this segment adds: those whose step lies in it (the drain
-        // after the K loop moves the window to the items past KT).
-        int wlo = g0, whi = min(g1, W);
+        // after the K loop moves the window to the items past KT).  The
+        // phase shifts the tile's item steps; item w reads peer w/8 - phase
+        // (pbase is the peer array moved back by `phase` peers).
+        int wlo = max(g0, 8 * phase), whi = min(g1, 8 * phase + W);
+        const uint16_t *pbase = p.partials - (size_t)phase * p.M * p.N;
         // Item w into the 2 KiB of LDS at ls.
         auto peer_dma_at = [&](uint32_t ls, int w, int i, uint32_t pd_off, int pd_n) {
             const bool live_item = w >= wlo && w < whi;
-            const int pp = live_item ? (w >> 3) : 0;
+            const int pp = live_item ? (w >> 3) : phase;
             const int blk = m0 + wm * WM + 16 * i;
             const int start = max(blk, row_lo);
             const int rows = live_item ? max(row_hi - start, 0) : 0;
             const u32x4_t rp = make_rsrc4(
-                p.partials + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
+                pbase + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
             const uint32_t off = pd_off - (uint32_t)(start - blk) * N2;
             dma16(rp, ls, pd_n < p.N ? off : OOB);
             dma16(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);

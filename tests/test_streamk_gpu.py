@@ -39,6 +39,9 @@ SHAPES = [
     (1000, 776, 72, 8),      # 3 K-steps: every tile fits one workgroup's run
     (4096, 1552, 512, 8),    # 112 tiles
     (2304, 2560, 256, 4),    # 90 tiles
+    # Tiles split into 3+ chunks start their peer items at a per-tile step:
+    (300, 1040, 4096, 4),    # 10 tiles, 128 K-steps, 3 peers: 14 phases
+    (200, 600, 2560, 8),     # 3 ragged tiles, 80 K-steps, 7 peers: 4 phases
 ]
 
 
@@ -57,7 +60,7 @@ def test_ar_split_equals_whole(orc, M, N, K, R):
                                                     host_bits(xc["peers"]), R), "split vs oracle")
 
 
-@pytest.mark.parametrize("M,N,K,R", SHAPES[:3])
+@pytest.mark.parametrize("M,N,K,R", SHAPES[:3] + SHAPES[-2:])
 def test_rs_split_all_ranks(orc, M, N, K, R):
     log(f"stream-K RS M={M} N={N} K={K} R={R}")
     xc = wl.integer_inputs("rs", M, N, K, R, seed=M + 2 * K)
