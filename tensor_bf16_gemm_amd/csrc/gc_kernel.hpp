@@ -186,6 +186,16 @@ __device__ __forceinline__ void dma16(u32x4_t r, uint32_t lds, uint32_t off)
                  : "memory");
 }
 
+// As dma16, marked non-temporal (nt): streaming data read once, which the
+// caches should not keep at the expense of the A and B tiles.
+__device__ __forceinline__ void dma16_nt(u32x4_t r, uint32_t lds, uint32_t off)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(lds), "v"(off), "s"(r)
+                 : "memory");
+}
+
 // As dma16, with the system-coherent cache policy (sc0 sc1): the load misses
 // every cache, so it sees data another XCD wrote through to memory.
 __device__ __forceinline__ void dma16_sys(u32x4_t r, uint32_t lds, uint32_t off)
@@ -259,7 +269,8 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
     return x * base + (x < rem ? x : rem) + j;
 }
 
-template <int MODE>
+// PEER_NT: peer partials are loaded non-temporal (AR / RS).
+template <int MODE, bool PEER_NT>
 __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
     // One array per operand and stage: distinct LDS objects carry distinct
@@ -552,8 +563,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const u32x4_t rp = make_rsrc4(
                 pbase + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
             const uint32_t off = pd_off - (uint32_t)(start - blk) * N2;
-            dma16(rp, ls, pd_n < p.N ? off : OOB);
-            dma16(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
+            if constexpr (PEER_NT) {
+                dma16_nt(rp, ls, pd_n < p.N ? off : OOB);
+                dma16_nt(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
+            } else {
+                dma16(rp, ls, pd_n < p.N ? off : OOB);
+                dma16(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
+            }
         };
         auto peer_dma = [&](const uint8_t *slotbuf, int w, int i, uint32_t pd_off, int pd_n) {
             peer_dma_at(lds_addr(slotbuf) + (uint32_t)(wave * PSLOT), w, i, pd_off, pd_n);
