@@ -207,8 +207,11 @@ def cpu_model() -> str:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    # The clock settles within about 60 back-to-back launches at M=4096 (the
+    # first ones run at a higher clock, then the power limit pulls it down
+    # and it recovers): the default warmup runs past that transient.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample")
