@@ -104,6 +104,12 @@ typedef struct gc_peers {
        whole.  Results agree to rounding of the fp32 partial sums. */
     void *workspace;
     uint64_t workspace_bytes;
+    /* All calls, optional: output tile height in rows, 0 = chosen per
+       problem (256, or 224 where that gives the workgroups less work),
+       256 or 224 = forced; any other value is GC_EINVAL.  Results agree to
+       rounding of the fp32 sums (the peer partials are added at different
+       K-steps).  224-row tiles are never split along K. */
+    uint32_t tile_rows;
 } gc_peers;
 
 /*

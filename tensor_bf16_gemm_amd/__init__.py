@@ -45,6 +45,7 @@ class GcPeers(ctypes.Structure):
         ("max_spins", ctypes.c_uint32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_uint64),
+        ("tile_rows", ctypes.c_uint32),
     ]
 
 
@@ -148,7 +149,7 @@ def _stream(stream) -> int:
 
 
 def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None, workspace=None,
-            status=None):
+            status=None, tile_rows: int = 0):
     """GEMM-AR: out [M,N] = bf16(A.B + sum of partials [R-1,M,N])."""
     import torch
     M, K = A.shape
@@ -161,14 +162,14 @@ def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None, workspa
     _bf16("out", out, (M, N))
     wp, wb = _ws_fields(workspace, A.device)
     peers = GcPeers(partials=_ptr(partials), workspace=wp, workspace_bytes=wb,
-                    status=_ptr(status))
+                    status=_ptr(status), tile_rows=int(tile_rows))
     _check(lib().gemm_ar(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_ar")
     return out
 
 
 def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None, workspace=None,
-            status=None):
+            status=None, tile_rows: int = 0):
     """GEMM-RS: out [ceil(M/R), N] = this rank's rows of bf16(A.B + sum of partials);
     ws [M,N] receives bf16(A.B) on the rows this rank does not own."""
     import torch
@@ -184,14 +185,14 @@ def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None, wor
     _bf16("out", out, (P, N))
     wp, wb = _ws_fields(workspace, A.device)
     peers = GcPeers(partials=_ptr(partials), ws=_ptr(ws), workspace=wp, workspace_bytes=wb,
-                    status=_ptr(status))
+                    status=_ptr(status), tile_rows=int(tile_rows))
     _check(lib().gemm_rs(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_rs")
     return out
 
 
 def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: int,
-            max_spins: int = 0, stream=None, workspace=None):
+            max_spins: int = 0, stream=None, workspace=None, tile_rows: int = 0):
     """AG-GEMM: out [R*Ms, N] = bf16(concat(shards).B), A = this rank's shard [Ms,K].
     flags: int32 tensor [R] in device memory or pinned host memory (the kernel
     polls it with system-scope loads); status: int32 device tensor [1]."""
@@ -212,7 +213,7 @@ def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: 
     wp, wb = _ws_fields(workspace, A.device)
     peers = GcPeers(shards=_ptr(shards), flags=_ptr(flags), epoch=int(epoch) & 0xFFFFFFFF,
                     status=_ptr(status), max_spins=int(max_spins), workspace=wp,
-                    workspace_bytes=wb)
+                    workspace_bytes=wb, tile_rows=int(tile_rows))
     _check(lib().ag_gemm(_ptr(A), _ptr(B), Ms, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "ag_gemm")
     return out

@@ -13,7 +13,10 @@
 //
 // Tile: 256 x 256 outputs per workgroup of eight waves (two per SIMD) in a
 // 2 (m) x 4 (n) grid; each wave owns 128 x 64 outputs as 8 x 4 blocks of
-// v_mfma_f32_16x16x32_bf16.  K advances 32 per step through a ring of four
+// v_mfma_f32_16x16x32_bf16.  A second instance has 224-row tiles (7 x 4
+// blocks per wave), which the host picks where it fills the last round of
+// tiles better (at M=4096, N=6288: 475 tiles in two rounds of 256 instead of
+// 400 of the taller tiles, 12 % less work per workgroup).  K advances 32 per step through a ring of four
 // LDS stages (16 KiB of A + 16 KiB of B each), so the loads of a stage are
 // issued three steps before it is consumed.
 //
@@ -111,9 +114,12 @@ struct Args {
     uint32_t sk_max_spins;
 };
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 512;
+constexpr int BM = 256, BN = 256, BK = 32, NT = 512;  // BM: the taller of the two tiles
 constexpr int WAVES = NT / 64;             // 8: 2 (m) x 4 (n)
 constexpr int WM = 128, WN = 64, FM = 8, FN = 4;
+// Peer items are numbered in groups of 8 K-steps, one per row block slot;
+// with 7 row blocks per wave the eighth slot of each group is empty.
+constexpr int ITEMS_PER_GROUP = 8;
 constexpr int STAGES = 4;
 constexpr int A_BYTES = BM * BK * 2;       // 16 KiB per stage
 constexpr int B_BYTES = BK * BN * 2;       // 16 KiB per stage
@@ -270,9 +276,12 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
 }
 
 // PEER_NT: peer partials are loaded non-temporal (AR / RS).
-template <int MODE, bool PEER_NT>
+// FMT: row blocks of 16 per wave, 8 (256-row tiles) or 7 (224-row tiles).
+template <int MODE, bool PEER_NT, int FMT>
 __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
+    static_assert(FMT == 8 || FMT == 7, "row blocks per wave");
+    constexpr int FMt = FMT, WMt = 16 * FMT, BMt = 2 * WMt;
     // One array per operand and stage: distinct LDS objects carry distinct
     // alias scopes, so the compiler knows that the loads filling one stage
     // cannot alias the fragment reads of another and does not wait for them.
@@ -309,7 +318,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
     const int b_slot = lane & 31;
     // fragment reads
     const int fi = lane & 15, fg = lane >> 4;
-    const uint32_t a_frag = (uint32_t)(wm * WM * 64 + fi * 64 + ((fg ^ ((fi >> 1) & 3)) << 4));
+    const uint32_t a_frag = (uint32_t)(wm * WMt * 64 + fi * 64 + ((fg ^ ((fi >> 1) & 3)) << 4));
     const int fB = (fi >> 2) | ((fg & 1) << 2);
     // B^T block j of this wave is logical 32-byte chunk q = 4*wn + j.
     uint32_t b_frag_j[FN];
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int gh = min(p.group_m, p.tiles_m - gm0);
         const int mt = gm0 + in_g % gh;
         const int nt = in_g / gh;
-        const int m0 = mt * BM, n0 = nt * BN;
+        const int m0 = mt * BMt, n0 = nt * BN;
 
         // Every load of the previous segment has landed and every wave is
         // done reading its LDS stages before this segment's loads reuse them.
@@ -484,8 +493,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         uint32_t a_off[2], b_off[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+            // (rows of the stage past a 224-row tile load nothing)
             const int row = m0 + 16 * (2 * wave + j) + (lane >> 2);
-            a_off[j] = row < p.M ? ((uint32_t)row * (uint32_t)p.K + (uint32_t)(8 * a_c)) * 2u : OOB;
+            a_off[j] = 16 * (2 * wave + j) < BMt && row < p.M
+                           ? ((uint32_t)row * (uint32_t)p.K + (uint32_t)(8 * a_c)) * 2u
+                           : OOB;
             const int k = 4 * wave + 2 * j + (lane >> 5);
             const int fk = (k & 3) | (((k >> 3) & 1) << 2);
             const int n = n0 + 16 * ((b_slot >> 1) ^ fk) + 8 * (b_slot & 1);
@@ -537,13 +549,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // so rows outside [row_lo, row_hi) read as zero (rows below wrap past
         // 2^31); chunks past N are masked per lane on edge tiles.  Items
         // outside [wlo, whi) load nothing (an empty buffer).
-        const int pm_base = m0 + wm * WM + fi;
+        const int pm_base = m0 + wm * WMt + fi;
         const int pn_base = n0 + wn * WN + 4 * fg;
         const int row_lo = MODE == MODE_RS ? p.lo : 0;
         const int row_hi = MODE == MODE_RS ? p.hi : p.M;
         int W = 0;
-        if (PEERS && m0 < row_hi && m0 + BM > row_lo)
-            W = p.npeers * FM;
+        if (PEERS && m0 < row_hi && m0 + BMt > row_lo)
+            W = p.npeers * ITEMS_PER_GROUP;
         // chunk of instruction 0 is lane/16, of instruction 1 lane/16 + 4
         const int pd_n = n0 + wn * WN + 8 * (lane >> 4);
         const uint32_t pd_off = (uint32_t)(lane & 15) * N2 + (uint32_t)pd_n * 2u;
@@ -555,9 +567,9 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const uint16_t *pbase = p.partials - (size_t)phase * p.M * p.N;
         // Item w into the 2 KiB of LDS at ls.
         auto peer_dma_at = [&](uint32_t ls, int w, int i, uint32_t pd_off, int pd_n) {
-            const bool live_item = w >= wlo && w < whi;
+            const bool live_item = w >= wlo && w < whi && i < FMt;
             const int pp = live_item ? (w >> 3) : phase;
-            const int blk = m0 + wm * WM + 16 * i;
+            const int blk = m0 + wm * WMt + 16 * i;
             const int start = max(blk, row_lo);
             const int rows = live_item ? max(row_hi - start, 0) : 0;
             const u32x4_t rp = make_rsrc4(
@@ -579,14 +591,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // lanes of one ds_read_b64 pass read 256 contiguous bytes.
         const uint32_t pc_off = (uint32_t)(((fg >> 1) * 16 + fi) * 16 + 8 * (fg & 1));
 
-        f32x4_t acc[FM][FN];
+        f32x4_t acc[FMt][FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FMt; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-        auto read_frags = [&](const uint8_t *cA, bf16x8_t (&fa)[FN], bf16x8_t (&fb)[FM]) {
+        auto read_frags = [&](const uint8_t *cA, bf16x8_t (&fa)[FN], bf16x8_t (&fb)[FMt]) {
             const uint32_t sa = opaque(lds_addr(cA)), sb = sa + A_BYTES;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -599,12 +611,12 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             }
             const uint32_t ab = sa + afr;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FMt; ++i)
                 fb[i] = *lds_ptr<bf16x8_t>(ab + i * 16 * 64);
         };
-        auto mfmas = [&](const bf16x8_t (&fa)[FN], const bf16x8_t (&fb)[FM]) {
+        auto mfmas = [&](const bf16x8_t (&fa)[FN], const bf16x8_t (&fb)[FMt]) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FMt; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
@@ -655,14 +667,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                     uint8_t *sl = (u & 1) ? sP1 : sP0;
                     // ---- M(kt) ----
                     barrier_only();
-                    bf16x8_t fa[FN], fb[FM];
+                    bf16x8_t fa[FN], fb[FMt];
                     read_frags(cA, fa, fb);
                     dma_stage(kt + 3, nA, nB);
                     if (PEERS) {
                         // Item kt was issued in M(kt-2); after it came stage
                         // kt+2, item kt+1 and stage kt+3.
                         wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
-                        if (kt < whi) {
+                        if (u < FMt && kt < whi) {
                             u32x2_t pv[FN];
                             const uint32_t pb = opaque(lds_addr(sl)) + wave * PSLOT;
 #pragma unroll
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                                 pv[j] = *lds_ptr<u32x2_t>(pb + pc_off + j * 512);
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
-                                acc[u][j] += unpack_bf16x4(pv[j]);
+                                acc[u % FMt][j] += unpack_bf16x4(pv[j]);
                         }
                         wait_lgkmcnt0();  // slot read back before it is refilled
                         peer_dma(sl, kt + 2, (u + 2) & 7, pd_off, pd_n);
@@ -689,7 +701,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // Lane offsets for the rest of the segment, recomputed (see opaque_v).
         const int ln = opaque_v(lane);
         const int fi2 = ln & 15, fg2 = ln >> 4;
-        const int pm_base2 = m0 + wm * WM + fi2;
+        const int pm_base2 = m0 + wm * WMt + fi2;
         const int pn_base2 = n0 + wn * WN + 4 * fg2;
 
         // ---- stream-K: hand the partial over, or collect the partials ----
@@ -697,7 +709,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // bytes per lane per block, so every access is a full 1 KiB per wave.
         // (Buffer accesses: one lane offset plus a scalar block offset, so no
         // 64-bit address is held per block.)
-        const uint32_t part_lane = (uint32_t)((wave * FM * FN * 64 + ln) * 16);
+        const uint32_t part_lane = (uint32_t)((wave * FMt * FN * 64 + ln) * 16);
         auto part_rsrc = [&](int slot) {
             return make_rsrc(p.sk_part + (size_t)slot * PART_FLOATS, PART_FLOATS * 4u);
         };
@@ -706,7 +718,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             if (!bad) {
                 const __amdgpu_buffer_rsrc_t rp = part_rsrc(cur_unit());
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FMt; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(
@@ -718,7 +730,9 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         }
         if (bad)
             continue;                  // the last unit, but its own chunk is missing
-        if (split) {
+        // (224-row tiles are never split: the host uses them only with a
+        // full round of tiles or more)
+        if constexpr (FMt == FM) if (split) {
             // The last unit of the tile: every other unit has counted itself
             // in, so its partial is stored or about to be.  Lane 0 of each
             // wave waits for their flags; then each wave streams its own
@@ -824,12 +838,12 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const uint32_t reg = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
             for (int w0 = KT & ~7; w0 < W; w0 += 8) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FMt; ++i)
                     if (w0 + i >= KT)
                         peer_dma_at(reg + (uint32_t)(i * PSLOT), w0 + i, i, pd_off2, pd_n2);
                 wait_vmcnt<0>();
 #pragma unroll
-                for (int i = 0; i < FM; ++i) {
+                for (int i = 0; i < FMt; ++i) {
                     __builtin_amdgcn_sched_barrier(0);
                     if (w0 + i >= KT) {
                         u32x2_t pv[FN];
@@ -852,14 +866,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws, (uint32_t)p.M * N2);
             const int s0 = p.rank * p.P;   // first global row of the slice
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FMt; ++i) {
                 const int m = pm_base2 + 16 * i;
                 const bool in_slice = m >= s0 && m < s0 + p.P;
                 const bool to_ws = !in_slice && m < p.M;
                 const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn_base2 * 2u;
                 // The 16 rows of the block (uniform): all in the slice, all
                 // outside it, or straddling its edge (both stores, masked).
-                const int blk = m0 + wm * WM + 16 * i;
+                const int blk = m0 + wm * WMt + 16 * i;
                 const bool any_out = blk < s0 || blk + 16 > s0 + p.P;
                 const bool any_in = blk + 16 > s0 && blk < s0 + p.P;
 #pragma unroll
@@ -876,7 +890,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             uint16_t *ob = p.out + (MODE == MODE_AG ? (size_t)q * p.M * p.N : 0);
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)p.M * N2);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FMt; ++i) {
                 const int m = pm_base2 + 16 * i;
                 const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u;
 #pragma unroll

@@ -55,6 +55,8 @@ int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64
         return GC_OK;  // nothing to do; pointers may be NULL
     if (!peers || !out || !aligned16(out))
         return GC_EINVAL;
+    if (peers->tile_rows != 0 && peers->tile_rows != 224 && peers->tile_rows != 256)
+        return GC_EINVAL;
     // A and B are not read when K == 0 (the output is then the peer sum).
     if (K > 0 && (!A || !B || !aligned16(A) || !aligned16(B)))
         return GC_EINVAL;
@@ -106,19 +108,31 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return GC_EIO;
-    a.tiles_m = (a.m_rows + gc::BM - 1) / gc::BM;
+    // One 512-thread workgroup per CU (the kernel holds up to 160 KiB of
+    // LDS); a persistent workgroup walks its list of tiles and segments.
+    const int cus = cu_count(dev);
     a.tiles_n = (a.N + gc::BN - 1) / gc::BN;
-    const int64_t per = (int64_t)a.tiles_m * a.tiles_n;
-    const int64_t total = MODE == gc::MODE_AG ? per * a.R : per;
+    const int64_t shards = MODE == gc::MODE_AG ? a.R : 1;
+    auto tiles_for = [&](int64_t bm) { return (a.m_rows + bm - 1) / bm * a.tiles_n * shards; };
+    // Tile height: 256 rows, or 224 where the workgroups then get fewer
+    // rows of work, ceil(tiles / CUs) * height, by 3 % or more -- at M=4096,
+    // N=6288 on 256 CUs, 475 tiles of 224 rows fill two rounds where 400 of
+    // 256 rows also took two.  Only problems with a full round of tiles or
+    // more take 224 rows; smaller ones are split along K instead.
+    const int64_t t256 = tiles_for(256), t224 = tiles_for(224);
+    int bm = 256;
+    if (peers->tile_rows != 0)
+        bm = (int)peers->tile_rows;
+    else if (t256 >= cus && (t224 + cus - 1) / cus * 224 * 100 < (t256 + cus - 1) / cus * 256 * 97)
+        bm = 224;
+    const int64_t total = bm == 256 ? t256 : t224;
     if (total > INT32_MAX)
         return GC_ENOTSUP;
+    a.tiles_m = (a.m_rows + bm - 1) / bm;
     a.num_tiles = (int)total;
     a.group_m = 4;
     if (a.num_tiles == 0)
         return GC_OK;
-    // One 512-thread workgroup per CU (the kernel holds up to 160 KiB of
-    // LDS); a persistent workgroup walks its list of tiles and segments.
-    const int cus = cu_count(dev);
     const int kt = (a.K + gc::BK - 1) / gc::BK;
     // Peer items (AR, RS) take 8 * peers consecutive K-steps of a tile,
     // from its first step on; for tiles split into three or more K chunks,
@@ -141,7 +155,7 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     // last partial round, in any chunk size, was slower than running them
     // whole.
     const int rest = a.num_tiles;
-    if (peers->workspace && kt > 8 && a.num_tiles < cus &&
+    if (bm == 256 && peers->workspace && kt > 8 && a.num_tiles < cus &&
         peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus)) {
         // The tiles are split along K into units that run chunk by chunk, so
         // that concurrent units share A and B in L2.
@@ -164,11 +178,18 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
             grid = cus;
         }
     }
-    if (MODE != gc::MODE_AG && peer_nt)
-        hipLaunchKernelGGL((gc::gc_kernel<MODE, MODE != gc::MODE_AG>), dim3(grid), dim3(gc::NT), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((gc::gc_kernel<MODE, false>), dim3(grid), dim3(gc::NT), 0, stream, a);
+    constexpr bool NT_OK = MODE != gc::MODE_AG;
+    if (bm == 224) {
+        if (NT_OK && peer_nt)
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 7>), dim3(grid), dim3(gc::NT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 7>), dim3(grid), dim3(gc::NT), 0, stream, a);
+    } else {
+        if (NT_OK && peer_nt)
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 8>), dim3(grid), dim3(gc::NT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 8>), dim3(grid), dim3(gc::NT), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
 }
 
@@ -193,7 +214,7 @@ const char *gemm_coll_strerror(int code)
         return "success";
     case GC_EINVAL:
         return "invalid argument (NULL or misaligned pointer, R or rank out of range, negative "
-               "size, or N/K not a multiple of 8)";
+               "size, N/K not a multiple of 8, or tile_rows other than 0, 224 and 256)";
     case GC_ENOTSUP:
         return "shape not supported by this kernel set (a buffer of 2 GiB or more)";
     case GC_EIO:

@@ -52,7 +52,8 @@ def test_peers_struct_layout(tmp_path):
         "offsetof(gc_peers,partials),offsetof(gc_peers,ws),offsetof(gc_peers,shards),"
         "offsetof(gc_peers,flags),offsetof(gc_peers,epoch),offsetof(gc_peers,status),"
         "offsetof(gc_peers,max_spins),sizeof(gc_peers));"
-        "printf(\"%zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes));"
+        "printf(\"%zu %zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes),"
+        "offsetof(gc_peers,tile_rows));"
         "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
@@ -62,7 +63,7 @@ def test_peers_struct_layout(tmp_path):
     P = gc.GcPeers
     py_vals = [P.partials.offset, P.ws.offset, P.shards.offset, P.flags.offset, P.epoch.offset,
                P.status.offset, P.max_spins.offset, ctypes.sizeof(P), P.workspace.offset,
-               P.workspace_bytes.offset]
+               P.workspace_bytes.offset, P.tile_rows.offset]
     assert c_vals == py_vals
 
 
