@@ -674,7 +674,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                         // Item kt was issued in M(kt-2); after it came stage
                         // kt+2, item kt+1 and stage kt+3.
                         wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
-                        if (u < FMt && kt < whi) {
+                        if (u < FMt && kt >= wlo && kt < whi) {
                             u32x2_t pv[FN];
                             const uint32_t pb = opaque(lds_addr(sl)) + wave * PSLOT;
 #pragma unroll
