@@ -59,6 +59,8 @@ def algorithmic_bytes(w) -> int:
     P = -(-w.M // w.R)
     lo, hi = min(w.rank * P, w.M), min(w.rank * P + P, w.M)
     owned = hi - lo
+    if w.mode == "ar2":   # peers of the slice in; ws, out slice and R-1 peer slices out
+        return base + e * ((w.R - 1) * owned * w.N + (w.M - owned) * w.N + w.R * owned * w.N)
     return base + e * ((w.R - 1) * owned * w.N + P * w.N + (w.M - owned) * w.N)
 
 
@@ -74,6 +76,12 @@ def make_step(w, x):
         out = torch.empty((P, w.N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
         return lambda: gc.gemm_rs(x["A"], x["B"], x["peers"], ws, out, R=w.R, rank=w.rank)
+    if w.mode == "ar2":
+        out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        peer_out = torch.empty((w.R - 1, w.M, w.N), dtype=torch.bfloat16, device=dev)
+        return lambda: gc.gemm_ar_two_shot(x["A"], x["B"], x["peers"], ws, peer_out, out, R=w.R,
+                                           rank=w.rank)
     out = torch.empty((w.R * w.M, w.N), dtype=torch.bfloat16, device=dev)
     flags = torch.ones(w.R, dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)

@@ -12,6 +12,12 @@
  *   gemm_rs   GEMM-RS: the same sum, but this rank keeps only its own row
  *             slice (same page, 实现拆解 step 1 and the reduce_scatter branch
  *             of the test reference).
+ *   gemm_ar_two_shot
+ *             GEMM-AR by the pages' own data flow: each rank reduces its row
+ *             slice over the peers' partials and stores the reduced slice
+ *             into every rank's output (same page, 实现拆解 step 1: the
+ *             owner's local_M slice, then the multicast store); here one
+ *             rank's share, with the other ranks' outputs as local buffers.
  *   ag_gemm   AG-GEMM: the token shards of all ranks, concatenated along M,
  *             times B, with the shards consumed in ring order ("[Kimi-K3]
  *             AG-GEMM for Sequence Parallelism", Purpose and Implementation
@@ -110,6 +116,10 @@ typedef struct gc_peers {
        rounding of the fp32 sums (the peer partials are added at different
        K-steps).  224-row tiles are never split along K. */
     uint32_t tile_rows;
+    /* gemm_ar_two_shot: [R-1][M][N] stand-ins for the other ranks' outputs,
+       slot p for rank (p < rank ? p : p + 1); receives this rank's reduced
+       slice rows (see gemm_ar_two_shot).  Ignored by the other calls. */
+    gc_bf16 *peer_out;
 } gc_peers;
 
 /*
@@ -136,6 +146,23 @@ int gemm_ar(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
  */
 int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
             const gc_peers *peers, gc_bf16 *out, void *stream);
+
+/*
+ * GEMM-AR, two-shot: this rank's part of the pages' GEMM-AR data flow.
+ * Everything gemm_rs does (same P, slice and peers->ws), except that the
+ * reduced slice rows go to a full-height output and to every peer output:
+ *   out [M][N]: rows i in [r*P, min((r+1)*P, M)) receive
+ *               bf16(A[i].B + sum_p partials[p][i]); the other rows are left
+ *               untouched (their owners store them);
+ *   peers->peer_out [R-1][M][N] (required): the same rows receive the same
+ *               values in every slot, standing in for the stores into the
+ *               other ranks' outputs (the pages' multicast store; unicast
+ *               stores over xGMI on MI355X); other rows untouched;
+ *   peers->ws [M][N] (required): as gemm_rs.
+ * peers->partials [R-1][M][N] is read only on the owned rows.
+ */
+int gemm_ar_two_shot(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R,
+                     int rank, const gc_peers *peers, gc_bf16 *out, void *stream);
 
 /*
  * AG-GEMM.  Shard q has Ms rows; the global activation is the concatenation

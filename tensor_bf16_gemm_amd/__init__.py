@@ -20,7 +20,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_ar", "gemm_rs", "ag_gemm", "should_run", "strerror", "lib", "GcPeers",
+__all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "should_run", "strerror", "lib", "GcPeers",
            "workspace_bytes", "default_workspace",
            "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_TIMEOUT_BASE"]
 
@@ -46,6 +46,7 @@ class GcPeers(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_uint64),
         ("tile_rows", ctypes.c_uint32),
+        ("peer_out", ctypes.c_void_p),
     ]
 
 
@@ -62,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         sig = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(GcPeers), vp, vp]
-        for name in ("gemm_ar", "gemm_rs", "ag_gemm"):
+        for name in ("gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"):
             f = getattr(L, name)
             f.argtypes = sig
             f.restype = ctypes.c_int
@@ -188,6 +189,31 @@ def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None, wor
                     status=_ptr(status), tile_rows=int(tile_rows))
     _check(lib().gemm_rs(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_rs")
+    return out
+
+
+def gemm_ar_two_shot(A, B, partials, ws, peer_out, out=None, *, R: int, rank: int, stream=None,
+                     workspace=None, status=None, tile_rows: int = 0):
+    """GEMM-AR, two-shot: this rank's rows [r*P, min((r+1)*P, M)) of
+    bf16(A.B + sum of partials) go to out [M,N] and to every slot of
+    peer_out [R-1,M,N]; ws [M,N] receives bf16(A.B) on the other rows.  Rows
+    of out and peer_out outside the slice are left untouched."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    _bf16("A", A)
+    _bf16("B", B, (K, N))
+    _bf16("partials", partials, (R - 1, M, N))
+    _bf16("ws", ws, (M, N))
+    _bf16("peer_out", peer_out, (R - 1, M, N))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _bf16("out", out, (M, N))
+    wp, wb = _ws_fields(workspace, A.device)
+    peers = GcPeers(partials=_ptr(partials), ws=_ptr(ws), workspace=wp, workspace_bytes=wb,
+                    status=_ptr(status), tile_rows=int(tile_rows), peer_out=_ptr(peer_out))
+    _check(lib().gemm_ar_two_shot(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers),
+                                  _ptr(out), _stream(stream)), "gemm_ar_two_shot")
     return out
 
 

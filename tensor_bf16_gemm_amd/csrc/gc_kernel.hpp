@@ -3,6 +3,8 @@
 // One persistent kernel template serves the three modes:
 //   AR  out = bf16(acc + sum of the R-1 peer partials)          (all rows)
 //   RS  slice rows as AR into out; other valid rows bf16(acc) into ws
+//       (two-shot AR: the same, with the reduced slice rows stored into a
+//       full-height out and into each of the R-1 peer outputs)
 //   AG  out rows of shard q = bf16(acc); shards taken in ring order, each
 //       behind a ready flag polled in the kernel
 // (GEMM-AR / GEMM-RS: "[Kimi-K3] Extend GEMM-RS to GEMM-AR", 实现拆解 step 1
@@ -75,6 +77,7 @@ struct Args {
     const uint16_t *partials;  // AR/RS: [R-1][M][N]
     uint16_t *out;             // AR: [M][N]; RS: [P][N]; AG: [R*Ms][N]
     uint16_t *ws;              // RS: [M][N]
+    uint16_t *peer_out;        // RS as two-shot AR: [R-1][M][N], or null
     const uint16_t *shards;    // AG: [R][Ms][K]
     const uint32_t *flags;     // AG: [R]
     int32_t *status;           // AG
@@ -862,7 +865,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 
         // ---- epilogue: bf16 stores, 8 bytes per lane per block ----
         if (MODE == MODE_RS) {
-            const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out, (uint32_t)p.P * N2);
+            // Two-shot AR: out is [M][N] (slice rows at their own index, rows
+            // past M not stored) and the slice rows also go to every peer
+            // output; plain RS: out is the [P][N] slice.
+            const bool two = p.peer_out != nullptr;
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.out, (uint32_t)(two ? p.M : p.P) * N2);
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws, (uint32_t)p.M * N2);
             const int s0 = p.rank * p.P;   // first global row of the slice
 #pragma unroll
@@ -876,14 +883,28 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 const int blk = m0 + wm * WMt + 16 * i;
                 const bool any_out = blk < s0 || blk + 16 > s0 + p.P;
                 const bool any_in = blk + 16 > s0 && blk < s0 + p.P;
+                const bool slice_st = in_slice && (!two || m < p.M);
+                const uint32_t obase = two ? (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u : rbase;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const bool ok = pn_base2 + 16 * j < p.N;
                     const u32x2_t v = pack_bf16x4(acc[i][j]);
                     if (any_in)
-                        store8(ro, (ok && in_slice) ? rbase + 32u * j : OOB, v);
+                        store8(ro, (ok && slice_st) ? obase + 32u * j : OOB, v);
                     if (any_out)
                         store8(rw, (ok && to_ws) ? rbase + 32u * j : OOB, v);
+                }
+                if (two && any_in) {
+                    for (int q = 0; q < p.npeers; ++q) {
+                        const __amdgpu_buffer_rsrc_t rq =
+                            make_rsrc(p.peer_out + (size_t)q * p.M * p.N, (uint32_t)p.M * N2);
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            const bool ok = pn_base2 + 16 * j < p.N;
+                            store8(rq, (ok && slice_st) ? obase + 32u * j : OOB,
+                                   pack_bf16x4(acc[i][j]));
+                        }
+                    }
                 }
             }
         } else {

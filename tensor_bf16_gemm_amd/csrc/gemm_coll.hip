@@ -252,13 +252,16 @@ int gemm_ar(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
     return dispatch<gc::MODE_AR>(a, peers, (hipStream_t)stream);
 }
 
-int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
-            const gc_peers *peers, gc_bf16 *out, void *stream)
+// GEMM-RS, or (two_shot) the two-shot GEMM-AR that extends it.
+static int rs_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
+              const gc_peers *peers, gc_bf16 *out, void *stream, bool two_shot)
 {
     int err = check_common(A, B, M, N, K, R, rank, peers, out);
     if (err || M == 0 || N == 0)
         return err;
     if (!peers->partials || !aligned16(peers->partials) || !peers->ws || !aligned16(peers->ws))
+        return GC_EINVAL;
+    if (two_shot && (!peers->peer_out || !aligned16(peers->peer_out)))
         return GC_EINVAL;
     if (!fits(M, K) || !fits(K, N) || !fits(M, N))
         return GC_ENOTSUP;
@@ -279,6 +282,7 @@ int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
     a.partials = peers->partials;
     a.out = out;
     a.ws = peers->ws;
+    a.peer_out = two_shot ? peers->peer_out : nullptr;
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
@@ -291,6 +295,18 @@ int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
     a.m_rows = (int)(end > M ? end : M);
     a.status = peers->status;
     return dispatch<gc::MODE_RS>(a, peers, (hipStream_t)stream);
+}
+
+int gemm_rs(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
+            const gc_peers *peers, gc_bf16 *out, void *stream)
+{
+    return rs_common(A, B, M, N, K, R, rank, peers, out, stream, false);
+}
+
+int gemm_ar_two_shot(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R,
+                     int rank, const gc_peers *peers, gc_bf16 *out, void *stream)
+{
+    return rs_common(A, B, M, N, K, R, rank, peers, out, stream, true);
 }
 
 int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K, int R, int rank,

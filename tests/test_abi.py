@@ -33,7 +33,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert set(names) == {"gemm_ar", "gemm_rs", "ag_gemm", "gemm_coll_should_run",
+    assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "gemm_coll_should_run",
                           "gemm_coll_strerror", "gemm_coll_workspace_bytes"}, names
     out = subprocess.run(["nm", "-D", "--defined-only", gc.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -52,8 +52,8 @@ def test_peers_struct_layout(tmp_path):
         "offsetof(gc_peers,partials),offsetof(gc_peers,ws),offsetof(gc_peers,shards),"
         "offsetof(gc_peers,flags),offsetof(gc_peers,epoch),offsetof(gc_peers,status),"
         "offsetof(gc_peers,max_spins),sizeof(gc_peers));"
-        "printf(\"%zu %zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes),"
-        "offsetof(gc_peers,tile_rows));"
+        "printf(\"%zu %zu %zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes),"
+        "offsetof(gc_peers,tile_rows),offsetof(gc_peers,peer_out));"
         "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
@@ -63,7 +63,7 @@ def test_peers_struct_layout(tmp_path):
     P = gc.GcPeers
     py_vals = [P.partials.offset, P.ws.offset, P.shards.offset, P.flags.offset, P.epoch.offset,
                P.status.offset, P.max_spins.offset, ctypes.sizeof(P), P.workspace.offset,
-               P.workspace_bytes.offset, P.tile_rows.offset]
+               P.workspace_bytes.offset, P.tile_rows.offset, P.peer_out.offset]
     assert c_vals == py_vals
 
 
@@ -86,17 +86,22 @@ PA = 0x7F0000000000
 
 def call(L, name, A=PA, B=PA + 0x100000, M=256, N=256, K=256, R=8, rank=0, out=PA + 0x200000,
          partials=PA + 0x300000, ws=PA + 0x400000, shards=PA + 0x500000, flags=PA + 0x600000,
-         status=PA + 0x600100, peers=True):
-    p = gc.GcPeers(partials=partials, ws=ws, shards=shards, flags=flags, epoch=1, status=status)
+         status=PA + 0x600100, peer_out=PA + 0x700000, tile_rows=0, peers=True):
+    p = gc.GcPeers(partials=partials, ws=ws, shards=shards, flags=flags, epoch=1, status=status,
+                   peer_out=peer_out, tile_rows=tile_rows)
     return getattr(L, name)(A, B, M, N, K, R, rank, ctypes.byref(p) if peers else None, out, None)
 
 
-@pytest.mark.parametrize("name", ["gemm_ar", "gemm_rs", "ag_gemm"])
+ALL = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"]
+
+
+@pytest.mark.parametrize("name", ALL)
 @pytest.mark.parametrize("kw", [
     dict(R=3), dict(R=1), dict(R=32), dict(R=6), dict(rank=8), dict(rank=-1),
     dict(M=-1), dict(N=-8), dict(K=-8), dict(N=12), dict(K=20),
     dict(out=None), dict(A=None), dict(B=None), dict(peers=False),
     dict(A=PA + 8), dict(B=PA + 0x100000 + 2), dict(out=PA + 0x200000 + 4),
+    dict(tile_rows=128), dict(tile_rows=1),
 ], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
 def test_invalid_arguments(L, name, kw):
     assert call(L, name, **kw) == gc.GC_EINVAL
@@ -107,19 +112,21 @@ def test_invalid_arguments(L, name, kw):
     ("gemm_rs", dict(partials=None)), ("gemm_rs", dict(ws=None)), ("gemm_rs", dict(ws=PA + 2)),
     ("ag_gemm", dict(shards=None)), ("ag_gemm", dict(flags=None)), ("ag_gemm", dict(flags=PA + 2)),
     ("ag_gemm", dict(status=None)), ("ag_gemm", dict(shards=PA + 0x500004)),
+    ("gemm_ar_two_shot", dict(partials=None)), ("gemm_ar_two_shot", dict(ws=None)),
+    ("gemm_ar_two_shot", dict(peer_out=None)), ("gemm_ar_two_shot", dict(peer_out=PA + 0x700002)),
 ])
 def test_invalid_peer_fields(L, name, kw):
     assert call(L, name, **kw) == gc.GC_EINVAL
 
 
-@pytest.mark.parametrize("name", ["gemm_ar", "gemm_rs", "ag_gemm"])
+@pytest.mark.parametrize("name", ALL)
 def test_oversized_buffers_not_supported(L, name):
     # A of 2^31 bytes cannot be addressed with 32-bit buffer offsets
     assert call(L, name, M=1 << 20, K=1 << 10) == gc.GC_ENOTSUP
     assert call(L, name, K=1 << 20, N=1 << 10) == gc.GC_ENOTSUP
 
 
-@pytest.mark.parametrize("name", ["gemm_ar", "gemm_rs", "ag_gemm"])
+@pytest.mark.parametrize("name", ALL)
 def test_empty_problem_launches_nothing(L, name):
     # M == 0 or N == 0: valid, nothing to do, pointers may be NULL
     assert call(L, name, M=0, A=None, out=None, peers=False) == gc.GC_OK

@@ -27,7 +27,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str            # "ar" | "rs" | "ag"
+    mode: str            # "ar" | "rs" | "ag" | "ar2" (GEMM-AR by the two-shot flow)
     M: int               # rows (AG: rows per shard, Ms)
     N: int
     K: int
@@ -67,6 +67,8 @@ WORKLOADS: dict[str, Workload] = {
                  "KDA projection M=1024, GEMM-AR"),
         Workload("kda4096_ar", "ar", 4096, 6288, 7168, 8, 0, 1.0, _isqrt(7168), 1.0, 0,
                  "KDA projection M=4096, GEMM-AR (headline)"),
+        Workload("kda4096_ar2", "ar2", 4096, 6288, 7168, 8, 0, 1.0, _isqrt(7168), 1.0, 0,
+                 "KDA projection M=4096, GEMM-AR by the two-shot flow (rank 0's share)"),
         Workload("ag_kda", "ag", 4096, 6288, 7168, 8, 3, 1.0, _isqrt(7168), 1.0, 0,
                  "AG-GEMM KDA, 8 shards of 4096 rows, ring from rank 3"),
         Workload("rs_odd", "rs", 32768 + 37, 7168, 896, 8, 5, _isqrt(896), _isqrt(896), 1.0, 0,
