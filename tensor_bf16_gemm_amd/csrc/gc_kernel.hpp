@@ -96,25 +96,25 @@ struct Args {
     int tiles_m, tiles_n;      // per shard for AG
     int num_tiles;             // total (AG: R * tiles_m * tiles_n)
     int group_m;               // row tiles per L2 group
-    // Work split.  The first dp_tiles tiles are taken whole, round by round.
-    // Each of the remaining sk_tiles is cut along K into sk_q chunks of
-    // sk_chunk steps (a multiple of 8; the last may be shorter), giving
-    // sk_units = sk_q * sk_tiles units numbered chunk-major (unit u is chunk
-    // u / sk_tiles of tile u % sk_tiles), dealt round-robin to the
-    // workgroups: the workgroups of one round run the same K range of
-    // neighbouring tiles, so they keep sharing A and B in L2.  A unit that
-    // finishes counts itself in sk_count[tile]; the last of a tile's units
-    // adds the others' fp32 partials and writes the tile, the others leave
-    // their partial in sk_part[u] and raise sk_flags[u].  Nobody waits for a
-    // unit that has not yet counted itself in, so the scheme cannot
-    // deadlock whatever the order in which workgroups get a CU.
+    // Work split.  A launch either takes dp_tiles whole tiles, round by
+    // round, or (dp_tiles == 0) cuts each of sk_tiles tiles along K into
+    // sk_q <= 16 chunks of sk_chunk steps (a multiple of 8; the last may be
+    // shorter), giving sk_units = sk_q * sk_tiles units numbered chunk-major
+    // (unit u is chunk u / sk_tiles of tile u % sk_tiles), one per workgroup:
+    // the workgroups of one XCD run the same K range of neighbouring tiles.
+    // The units of a tile exchange fp32 partials through sk_part[u] and
+    // finish the tile in shares (see the kernel).  Counters, flags and
+    // claims hold the launch epoch, so none of them is ever reset.
     int dp_tiles;
     int sk_tiles, sk_q, sk_chunk, sk_units;
     unsigned long long *sk_count;  // [sk_tiles]: (epoch << 32) | arrivals
+    uint32_t *sk_claim;        // [sk_tiles][16]: epoch of the launch that claimed the share
     uint32_t *sk_flags;        // [2 * sk_units]: epoch, partial valid
     float *sk_part;            // [sk_units][BM*BN]
     uint32_t sk_epoch;
-    uint32_t sk_max_spins;
+    uint32_t sk_max_spins;     // guard on waits that always end
+    uint32_t sk_wait_spins;    // how long a unit waits for its tile's other units
+    uint32_t sk_grace_spins;   // how long the last unit leaves the others to claim
 };
 
 constexpr int BM = 256, BN = 256, BK = 32, NT = 512;  // BM: the taller of the two tiles
@@ -206,12 +206,14 @@ __device__ __forceinline__ void dma16_nt(u32x4_t r, uint32_t lds, uint32_t off)
 }
 
 // As dma16, with the system-coherent cache policy (sc0 sc1): the load misses
-// every cache, so it sees data another XCD wrote through to memory.
-__device__ __forceinline__ void dma16_sys(u32x4_t r, uint32_t lds, uint32_t off)
+// every cache, so it sees data another XCD wrote through to memory.  The
+// offset is a lane part plus a scalar part (soffset), so that a run of loads
+// at different block offsets needs one lane register, not one per block.
+__device__ __forceinline__ void dma16_sys(u32x4_t r, uint32_t lds, uint32_t voff, uint32_t soff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc0 sc1 lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc0 sc1 lds"
                  :
-                 : "s"(lds), "v"(off), "s"(r)
+                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
                  : "memory");
 }
 
@@ -280,10 +282,15 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
 
 // PEER_NT: peer partials are loaded non-temporal (AR / RS).
 // FMT: row blocks of 16 per wave, 8 (256-row tiles) or 7 (224-row tiles).
-template <int MODE, bool PEER_NT, int FMT>
+// SPLIT: the launch runs split units only (dp_tiles == 0); otherwise whole
+// tiles only, and the hand-over code is not compiled in.  (Each instance then
+// gets a register allocation of its own: the hand-over's registers do not
+// weigh on the whole-tile K loop, nor the reverse.)
+template <int MODE, bool PEER_NT, int FMT, bool SPLIT>
 __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
     static_assert(FMT == 8 || FMT == 7, "row blocks per wave");
+    static_assert(!SPLIT || FMT == 8, "224-row tiles are never split");
     constexpr int FMt = FMT, WMt = 16 * FMT, BMt = 2 * WMt;
     // One array per operand and stage: distinct LDS objects carry distinct
     // alias scopes, so the compiler knows that the loads filling one stage
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
     for (;;) {
         int L, g0, g1, phase;
         bool bad = false;
-        if (dp_lin < p.dp_tiles) {
+        if (!SPLIT && dp_lin < p.dp_tiles) {
             const int lin = dp_lin;
             const int live = min(G, p.dp_tiles - lin);
             dp_lin = live < G ? p.dp_tiles : lin + G;   // no overflow past dp_tiles
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             g0 = 0;
             g1 = KT;
             phase = 0;
-        } else if (unit < p.sk_units) {
+        } else if (SPLIT && unit < p.sk_units) {
             const int c = unit / p.sk_tiles;
             g0 = c * p.sk_chunk;
             g1 = min(KT, g0 + p.sk_chunk);
@@ -389,43 +396,10 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             bfj[j] = (uint32_t)opaque_v((int)b_frag_j[j]);
         const uint32_t afr = (uint32_t)opaque_v((int)a_frag);
 
-        // The split unit being run (derived from the loop state instead of
-        // being kept live across the K loop): whole tiles come first, so
-        // `unit` has moved past v exactly when a unit is running.
-        const bool split = unit != v && p.sk_q > 1;
+        // In a split launch every segment is a split unit, unit - G (derived
+        // from the loop state instead of being kept live across the K loop).
+        const bool split = SPLIT && p.sk_q > 1;
         auto cur_unit = [&]() { return unit - G; };
-        auto cur_tile = [&]() { return (unit - G) % p.sk_tiles; };
-        // Count this unit in for its tile; returns (to every thread) how
-        // many of the tile's units, this one included, have arrived in this
-        // launch.  The counter holds the launch epoch in its upper half, so
-        // it never needs resetting.  The count is passed on through the
-        // first word of stage 0, once every load into the stages has landed
-        // and every read of them is done.
-        auto arrive = [&]() {
-            int *cell = (int *)sS0;
-            wait_vmcnt<0>();
-            barrier_only();
-            if (tid == 0) {
-                unsigned long long *ctr = p.sk_count + cur_tile();
-                unsigned long long cur =
-                    __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                unsigned long long nxt;
-                for (;;) {
-                    nxt = (uint32_t)(cur >> 32) == p.sk_epoch
-                              ? cur + 1
-                              : ((unsigned long long)p.sk_epoch << 32) | 1ull;
-                    if (__hip_atomic_compare_exchange_strong(ctr, &cur, nxt, __ATOMIC_RELAXED,
-                                                             __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_SYSTEM))
-                        break;
-                }
-                *cell = (int)(uint32_t)nxt;
-            }
-            __syncthreads();
-            const int n = *cell;
-            __syncthreads();
-            return n;
-        };
         // Raise the partial-ready flag of unit u (after its partial, if
         // any, is stored and written back).
         // Flags are two words per unit: [2u] the epoch of its last hand-over,
@@ -445,6 +419,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 wait_vmcnt<0>();
                 __hip_atomic_store(p.sk_flags + 2 * cur_unit(), p.sk_epoch, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_SYSTEM);
+                wait_vmcnt<0>();       // raised before the unit counts itself in
             }
         };
 
@@ -480,8 +455,8 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 if (!ok) {
                     // The tile cannot be finished.  A split unit still goes
                     // through the hand-over (with no K-steps and an invalid
-                    // partial) so that the tile's last unit does not wait
-                    // forever.
+                    // partial) so that the tile's other units do not wait
+                    // for it until their time-out.
                     if (!split)
                         continue;
                     bad = true;
@@ -707,120 +682,187 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int pm_base2 = m0 + wm * WMt + fi2;
         const int pn_base2 = n0 + wn * WN + 4 * fg2;
 
-        // ---- stream-K: hand the partial over, or collect the partials ----
-        // A partial is stored in accumulator order (wave, block, lane), 16
+        // ---- split tile: exchange partials, finish the tile in shares ----
+        // Each wave's 32 accumulator blocks form 16 segments, row block i and
+        // column half h (blocks (i, 2h) and (i, 2h+1)); share k of a tile's q
+        // units is segments [16k/q, 16(k+1)/q).  Every unit stores its whole
+        // fp32 partial, raises its flag and counts itself in on the tile's
+        // arrival counter.  A unit that is not the last to arrive waits a
+        // short, bounded time for the other units' flags; if they all come,
+        // it claims its own share.  The last to arrive (every partial is then
+        // stored) claims its own share, gives the other units a short time
+        // to claim theirs, and claims those still unclaimed.  A unit then
+        // finishes the shares it holds: it adds the other units' copies of
+        // their segments and stores them.  A share is claimed by a
+        // compare-and-swap of its word to the launch epoch, so exactly one
+        // unit finishes it.  Nobody waits without bound for a unit that has
+        // not arrived, so the scheme completes whatever the order in which
+        // workgroups get a CU; when they run at once, a tile's reduction is
+        // spread over all of its units, none of which reads more than about
+        // 1/q of each of the other partials.
+        // A partial is kept in accumulator order (wave, block, lane), 16
         // bytes per lane per block, so every access is a full 1 KiB per wave.
-        // (Buffer accesses: one lane offset plus a scalar block offset, so no
-        // 64-bit address is held per block.)
-        const uint32_t part_lane = (uint32_t)((wave * FMt * FN * 64 + ln) * 16);
-        auto part_rsrc = [&](int slot) {
-            return make_rsrc(p.sk_part + (size_t)slot * PART_FLOATS, PART_FLOATS * 4u);
-        };
-        if (split && arrive() < p.sk_q) {
-            // Not the last of the tile's units: hand the partial over.
+        uint32_t smask = (1u << (2 * FMt)) - 1u;   // segments to finish: all, for a whole tile
+        if constexpr (SPLIT) {
+            const int u = __builtin_amdgcn_readfirstlane(cur_unit());
+            const int sc = __builtin_amdgcn_readfirstlane(u / p.sk_tiles);
+            const int stt = u - sc * p.sk_tiles;
+            const int nq = p.sk_q;
+            const uint32_t lane16 = (uint32_t)ln * 16u;
+            const uint32_t wave_off = (uint32_t)(wave * FM * FN * 1024);
             if (!bad) {
-                const __amdgpu_buffer_rsrc_t rp = part_rsrc(cur_unit());
+                const __amdgpu_buffer_rsrc_t rp =
+                    make_rsrc(p.sk_part + (size_t)u * PART_FLOATS, PART_FLOATS * 4u);
 #pragma unroll
-                for (int i = 0; i < FMt; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)part_lane,
-                            (int)((i * FN + j) * 64 * 16), CPOL_SYS);
+                            __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)lane16,
+                            (int)(wave_off + (uint32_t)((i * FN + j) * 1024)), CPOL_SYS);
             }
             signal_partial(bad ? 0u : 1u);
-            continue;
-        }
-        if (bad)
-            continue;                  // the last unit, but its own chunk is missing
-        // (224-row tiles are never split: the host uses them only with a
-        // full round of tiles or more)
-        if constexpr (FMt == FM) if (split) {
-            // The last unit of the tile: every other unit has counted itself
-            // in, so its partial is stored or about to be.  Lane 0 of each
-            // wave waits for their flags; then each wave streams its own
-            // 32 KiB of every partial through 16 KiB of the (now idle) LDS
-            // stages, in quarters of 8 KiB kept two in flight, and adds them.
-            // (uniform; integer division is done in vector registers, and
-            // the buffer descriptors built from these must be scalar)
-            const int mine = __builtin_amdgcn_readfirstlane(cur_unit() / p.sk_tiles);
-            const int tt = __builtin_amdgcn_readfirstlane(cur_tile());
-            const int nparts = p.sk_q - 1;
-            auto slot = [&](int c) { return (c < mine ? c : c + 1) * p.sk_tiles + tt; };
-            int ok = 1;
-            if (lane == 0) {
-                for (int c = 0; c < nparts && ok; ++c) {
-                    const int vv = slot(c);
-                    uint32_t spins = 0;
+            // Wave 0 counts the unit in, watches the other units' flags and
+            // claim words (one lane per unit) and claims; the verdict goes to
+            // every wave through the first word of stage 0 (every wave's
+            // stage loads have landed and its stage reads are done:
+            // signal_partial waited for them).
+            int *cell = (int *)sS0;
+            if (wave == 0) {
+                int n = 0;
+                if (lane == 0) {
+                    unsigned long long *ctr = p.sk_count + stt;
+                    unsigned long long cur =
+                        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    unsigned long long nxt;
                     for (;;) {
-                        uint32_t f = __hip_atomic_load(p.sk_flags + 2 * vv, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_SYSTEM);
+                        nxt = (uint32_t)(cur >> 32) == p.sk_epoch
+                                  ? cur + 1
+                                  : ((unsigned long long)p.sk_epoch << 32) | 1ull;
+                        if (__hip_atomic_compare_exchange_strong(ctr, &cur, nxt, __ATOMIC_RELAXED,
+                                                                 __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_SYSTEM))
+                            break;
+                    }
+                    n = (int)(uint32_t)nxt;
+                }
+                const bool lst = __builtin_amdgcn_readlane(n, 0) >= nq;
+                const bool act = lane < nq - 1;
+                const int cp = lane < sc ? lane : lane + 1;
+                const uint32_t *fl = p.sk_flags + 2 * (act ? cp * p.sk_tiles + stt : 0);
+                // The last unit finds every flag raised; the limit there is
+                // only a guard.
+                const uint32_t limit = lst ? p.sk_max_spins : p.sk_wait_spins;
+                bool done = !act, valid = true;
+                uint32_t spins = 0;
+                for (;;) {
+                    if (!done) {
+                        const uint32_t f = __hip_atomic_load(fl, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_SYSTEM);
                         if ((int32_t)(f - p.sk_epoch) >= 0) {
-                            ok = (int)__hip_atomic_load(p.sk_flags + 2 * vv + 1, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_SYSTEM);
-                            break;
+                            done = true;
+                            valid = __hip_atomic_load(fl + 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_SYSTEM) != 0;
                         }
-                        if (++spins >= p.sk_max_spins) {
-                            if (p.status)
-                                atomicCAS(p.status, 0, 1000 + 16);
-                            ok = 0;
+                    }
+                    if (__builtin_amdgcn_ballot_w64(!done) == 0)
+                        break;
+                    if (++spins >= limit) {
+                        if (lst && lane == 0 && p.status)
+                            atomicCAS(p.status, 0, 1000 + 16);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                const bool all = __builtin_amdgcn_ballot_w64(!(done && valid)) == 0 && !bad;
+                // Claims: lane k acts for share k.
+                uint32_t *cw = p.sk_claim + stt * 16 + (lane < nq ? lane : 0);
+                auto claim = [&](bool want) {
+                    bool got = false;
+                    if (want) {
+                        uint32_t cur = __hip_atomic_load(cw, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_SYSTEM);
+                        got = cur != p.sk_epoch &&
+                              __hip_atomic_compare_exchange_strong(cw, &cur, p.sk_epoch,
+                                                                   __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_SYSTEM);
+                    }
+                    return __builtin_amdgcn_ballot_w64(got);
+                };
+                uint64_t won = all ? claim(lane == sc) : 0;
+                if (all && lst) {
+                    // Give the other units a short time to claim their shares.
+                    bool settled = !(lane < nq && lane != sc);
+                    uint32_t gspins = 0;
+                    for (;;) {
+                        if (!settled)
+                            settled = __hip_atomic_load(cw, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_SYSTEM) == p.sk_epoch;
+                        if (__builtin_amdgcn_ballot_w64(!settled) == 0 || ++gspins >= p.sk_grace_spins)
                             break;
-                        }
                         __builtin_amdgcn_s_sleep(2);
                     }
+                    won |= claim(!settled);
                 }
+                uint32_t m = 0;
+                for (int k = 0; k < nq; ++k)
+                    if ((won >> k) & 1u)
+                        m |= (1u << (16 * (k + 1) / nq)) - (1u << (16 * k / nq));
+                if (lane == 0)
+                    *cell = (int)m;
             }
-            ok = __builtin_amdgcn_readfirstlane(ok);
-            // Every wave's stage loads (also the out-of-range ones past the
-            // segment, which still write LDS) have landed, and its stage
-            // reads are done, before the stages are reused.  All waves meet
-            // here, also one whose partner failed.
-            wait_vmcnt<0>();
-            barrier_only();
-            if (!ok)
-                continue;              // a partner failed: leave the tile unwritten
+            __syncthreads();
+            smask = (uint32_t)__builtin_amdgcn_readfirstlane(*cell);
+            __syncthreads();
+            if (smask == 0)
+                continue;              // nothing to finish here
+            // Add the other units' copies of the segments in smask: items t =
+            // (unit t / ns, t % ns-th segment of smask) of 2 KiB per wave,
+            // through a ring of eight 2 KiB slots in the wave's 16 KiB of the
+            // idle stages, DEPTH items in flight.  Items past the end are
+            // loads from an empty range (they fill their slot with zeros).
+            const int ns = __builtin_popcount(smask);
+            const int T = (nq - 1) * ns;
             const uint8_t *wst = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1
                                : (wave >> 1) == 2 ? sS2 : sS3;
-            const uint32_t half0 = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
-            const u32x4_t none = make_rsrc4(p.sk_part, 0u);
-            auto prt = [&](int c) {
-                return c < nparts ? make_rsrc4(p.sk_part + (size_t)slot(c) * PART_FLOATS,
-                                               PART_FLOATS * 4u)
-                                  : none;
+            const uint32_t ring = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
+            auto seg_of = [&](int k) {     // k-th segment (from 0) of smask
+                uint32_t mm = smask;
+                for (int r = 0; r < k; ++r)
+                    mm &= mm - 1u;
+                return __builtin_ctz(mm);
             };
-            // quarter q of a partial: blocks 8q .. 8q+7 (row blocks 2q, 2q+1)
-            auto load_q = [&](u32x4_t r, int q, uint32_t dst) {
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    dma16_sys(r, dst + (uint32_t)(b * 1024),
-                              (uint32_t)(wave * FM * FN * 64 * 16 + (8 * q + b) * 1024) +
-                                  (uint32_t)lane * 16u);
+            constexpr int DEPTH = 6;
+            auto issue = [&](int t) {
+                const int pc = t / ns;
+                const int cp = pc < sc ? pc : pc + 1;
+                const int sg = seg_of(t - pc * ns);
+                const u32x4_t r = make_rsrc4(p.sk_part + (size_t)(cp * p.sk_tiles + stt) * PART_FLOATS,
+                                             t < T ? PART_FLOATS * 4u : 0u);
+                const uint32_t slot = ring + (uint32_t)((t & 7) * 2048);
+                const uint32_t so = wave_off + (uint32_t)(sg * 2048);
+                dma16_sys(r, slot, lane16, so);
+                dma16_sys(r, slot + 1024u, lane16, so + 1024u);
             };
-            u32x4_t rc = prt(0);
-            load_q(rc, 0, half0);
-            load_q(rc, 1, half0 + 8192);
-            for (int c = 0; c < nparts; ++c) {
-                const u32x4_t rn = prt(c + 1);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t h = half0 + (uint32_t)((q & 1) * 8192);
-                    wait_vmcnt<8>();           // this quarter landed
-                    u32x4_t bl[8];
+            for (int t = 0; t < DEPTH; ++t)
+                issue(t);
+            for (int t = 0; t < T; ++t) {
+                wait_vmcnt<2 * (DEPTH - 1)>();   // item t landed
+                const uint32_t slot = ring + (uint32_t)((t & 7) * 2048);
+                const u32x4_t x0 = *lds_ptr<u32x4_t>(slot + lane16);
+                const u32x4_t x1 = *lds_ptr<u32x4_t>(slot + 1024u + lane16);
+                wait_lgkmcnt0();
+                const int sg = seg_of(t % ns);
 #pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        bl[b] = *lds_ptr<u32x4_t>(h + (uint32_t)(b * 1024 + lane * 16));
-                    wait_lgkmcnt0();
-#pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        acc[2 * q + (b >> 2)][b & 3] += __builtin_bit_cast(f32x4_t, bl[b]);
-                    // refill this half with the quarter two ahead
-                    if (q < 2)
-                        load_q(rc, q + 2, h);
-                    else
-                        load_q(rn, q - 2, h);
-                }
-                rc = rn;
+                for (int s2 = 0; s2 < 2 * FM; ++s2)
+                    if (sg == s2) {
+                        acc[s2 >> 1][2 * (s2 & 1)] += __builtin_bit_cast(f32x4_t, x0);
+                        acc[s2 >> 1][2 * (s2 & 1) + 1] += __builtin_bit_cast(f32x4_t, x1);
+                    }
+                issue(t + DEPTH);
             }
+            wait_vmcnt<0>();
         }
 
         // ---- peer items the K loop did not reach: eight per round trip ----
@@ -828,7 +870,9 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // each wave stages the up to 8 items of a row-block group in its
         // 16 KiB of the idle LDS stages, once every wave's stage loads have
         // landed and its stage reads are done.
-        if (PEERS && W > KT) {
+        // (A split launch has every item inside the K loop: the host splits
+        // only when 8 * npeers <= KT.)
+        if (!SPLIT && PEERS && W > KT) {
             wait_vmcnt<0>();
             barrier_only();
             wlo = KT;
@@ -864,6 +908,9 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         }
 
         // ---- epilogue: bf16 stores, 8 bytes per lane per block ----
+        // (of the owned segments only: in a split tile, the other units
+        // store the rest)
+        auto own = [&](int i, int j) { return ((smask >> (2 * i + (j >> 1))) & 1u) != 0; };
         if (MODE == MODE_RS) {
             // Two-shot AR: out is [M][N] (slice rows at their own index, rows
             // past M not stored) and the slice rows also go to every peer
@@ -887,7 +934,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 const uint32_t obase = two ? (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u : rbase;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const bool ok = pn_base2 + 16 * j < p.N;
+                    const bool ok = pn_base2 + 16 * j < p.N && own(i, j);
                     const u32x2_t v = pack_bf16x4(acc[i][j]);
                     if (any_in)
                         store8(ro, (ok && slice_st) ? obase + 32u * j : OOB, v);
@@ -900,7 +947,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                             make_rsrc(p.peer_out + (size_t)q * p.M * p.N, (uint32_t)p.M * N2);
 #pragma unroll
                         for (int j = 0; j < FN; ++j) {
-                            const bool ok = pn_base2 + 16 * j < p.N;
+                            const bool ok = pn_base2 + 16 * j < p.N && own(i, j);
                             store8(rq, (ok && slice_st) ? obase + 32u * j : OOB,
                                    pack_bf16x4(acc[i][j]));
                         }
@@ -916,7 +963,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const bool ok = m < p.M && pn_base2 + 16 * j < p.N;
+                    const bool ok = m < p.M && pn_base2 + 16 * j < p.N && own(i, j);
                     store8(ro, ok ? rbase + 32u * j : OOB, pack_bf16x4(acc[i][j]));
                 }
             }

@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "gc_kernel.hpp"
@@ -14,7 +15,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];      // 0 = not queried yet
-std::atomic<uint32_t> g_epoch[kMaxDevices];    // stream-K launch counter
+std::atomic<uint32_t> g_epoch[kMaxDevices];    // split-launch counter
 
 int cu_count(int dev)
 {
@@ -63,43 +64,36 @@ int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64
     return GC_OK;
 }
 
-// Workspace layout for G workgroups: one 8-byte arrival counter per split
-// tile (fewer than G of them), two flag words per split unit, then one fp32
-// partial tile per split unit; at most 2 G units.  Each part starts on a
-// 256-byte boundary.
-constexpr int kMaxUnitsPerGroup = 2;
+// Workspace layout for G workgroups (at most G split units, one per
+// workgroup, and fewer than G split tiles): an 8-byte arrival counter and 16
+// claim words per tile, two flag words per unit, then one fp32 partial tile
+// per unit.  Each part starts on a 256-byte boundary.
 int64_t a256(int64_t x) { return (x + 255) / 256 * 256; }
 int64_t count_bytes(int groups) { return a256((int64_t)groups * 8); }
-int64_t flag_bytes(int groups) { return a256((int64_t)groups * kMaxUnitsPerGroup * 8); }
+int64_t claim_bytes(int groups) { return a256((int64_t)groups * 16 * 4); }
+int64_t flag_bytes(int groups) { return a256((int64_t)groups * 8); }
 int64_t workspace_bytes_for(int groups)
 {
-    return count_bytes(groups) + flag_bytes(groups) +
-           (int64_t)groups * kMaxUnitsPerGroup * gc::PART_FLOATS * 4;
+    return count_bytes(groups) + claim_bytes(groups) + flag_bytes(groups) +
+           (int64_t)groups * gc::PART_FLOATS * 4;
 }
 
-// Chunk size for the sk_tiles tiles left after the full rounds (sk_tiles <
-// groups), from a cost model in K-step units: the units run in
-// ceil(q * sk_tiles / groups) rounds of `chunk` steps plus a fixed cost per
-// unit (pipeline fill and drain, the partial hand-over), and the last unit
-// of each tile reads q - 1 partials.  Returns `kt` (no split) when splitting
-// does not pay.
-int pick_chunk(int kt, int sk_tiles, int groups)
+// Chunk size (K-steps, a multiple of 8) for a problem of `tiles` < groups
+// tiles: the smallest that cuts each tile into at most min(16, groups /
+// tiles) chunks, so that the units fill as many workgroups as they can in
+// one round.  Every unit of a tile reads at most 1/q of each of the q - 1
+// other partials, so the hand-over costs about the same whatever q is, and
+// the shortest chunks win (measured at M = 256, N = 3648, K = 7168, 15
+// tiles: 14 chunks of 16 steps against 7 of 32).  Returns `kt` (no split)
+// when fewer than two chunks fit.
+int pick_chunk(int kt, int tiles, int groups)
 {
-    constexpr int kFill = 4, kHandOver = 4, kPartial = 8;
-    int best = kt, best_cost = kt + kFill;
-    for (int chunk = 8; chunk < kt; chunk += 8) {
-        const int q = (kt + chunk - 1) / chunk;
-        const int64_t units = (int64_t)q * sk_tiles;
-        if (units > (int64_t)kMaxUnitsPerGroup * groups)
-            continue;
-        const int rounds = (int)((units + groups - 1) / groups);
-        const int cost = rounds * (chunk + kFill + kHandOver) + kPartial * (q - 1);
-        if (cost < best_cost) {
-            best_cost = cost;
-            best = chunk;
-        }
-    }
-    return best;
+    const int qmax = std::min(16, groups / tiles);
+    if (qmax < 2)
+        return kt;
+    int chunk = (kt + qmax - 1) / qmax;
+    chunk = (chunk + 7) / 8 * 8;
+    return chunk < kt ? chunk : kt;
 }
 
 template <int MODE>
@@ -153,42 +147,54 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     // Only problems with fewer tiles than workgroups are split along K:
     // measured at M=4096 (400 tiles on 256 CUs), splitting the tiles of the
     // last partial round, in any chunk size, was slower than running them
-    // whole.
-    const int rest = a.num_tiles;
-    if (bm == 256 && peers->workspace && kt > 8 && a.num_tiles < cus &&
+    // whole.  A split launch needs every peer item inside the K loop
+    // (8 * npeers <= kt).
+    const int npeer_steps = MODE == gc::MODE_AG ? 0 : 8 * a.npeers;
+    if (bm == 256 && peers->workspace && kt > 8 && a.num_tiles < cus && npeer_steps <= kt &&
         peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus)) {
-        // The tiles are split along K into units that run chunk by chunk, so
-        // that concurrent units share A and B in L2.
-        const int chunk = pick_chunk(kt, rest, cus);
-        const int64_t units = (int64_t)((kt + chunk - 1) / chunk) * rest;
-        if (chunk < kt && units <= (int64_t)kMaxUnitsPerGroup * cus) {
+        const int chunk = pick_chunk(kt, a.num_tiles, cus);
+        if (chunk < kt) {
             char *ws = (char *)peers->workspace;
-            a.dp_tiles = a.num_tiles - rest;
-            a.sk_tiles = rest;
+            a.dp_tiles = 0;
+            a.sk_tiles = a.num_tiles;
             a.sk_chunk = chunk;
             a.sk_q = (kt + chunk - 1) / chunk;
-            a.sk_units = a.sk_q * rest;
+            a.sk_units = a.sk_q * a.num_tiles;
             a.sk_count = (unsigned long long *)ws;
-            a.sk_flags = (uint32_t *)(ws + count_bytes(cus));
-            a.sk_part = (float *)(ws + count_bytes(cus) + flag_bytes(cus));
+            a.sk_claim = (uint32_t *)(ws + count_bytes(cus));
+            a.sk_flags = (uint32_t *)(ws + count_bytes(cus) + claim_bytes(cus));
+            a.sk_part = (float *)(ws + count_bytes(cus) + claim_bytes(cus) + flag_bytes(cus));
             a.sk_epoch = g_epoch[dev < kMaxDevices ? dev : 0].fetch_add(1) + 1;
             a.sk_max_spins = 1u << 22;
+            // About 0.3 ms of polling: far more than the spread of the
+            // units' arrival times when they run at once (measured: up to
+            // 25 us), short when they do not.
+            a.sk_wait_spins = 256;
+            // The last unit to arrive leaves the others about 30 us to claim
+            // their shares (they see its flag and claim within a few us)
+            // before it claims what is left.
+            a.sk_grace_spins = 32;
             if (MODE != gc::MODE_AG && a.npeers > 0 && kt / 8 >= a.npeers && a.sk_q >= 3)
                 a.peer_phases = kt / 8 - a.npeers + 1;
-            grid = cus;
+            grid = a.sk_units;
         }
     }
     constexpr bool NT_OK = MODE != gc::MODE_AG;
-    if (bm == 224) {
+    if (a.sk_units > 0) {
+        // Every tile is split (dp_tiles == 0), one unit per workgroup.  (The
+        // peer set of so few tiles is far below the non-temporal threshold.)
+        hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 8, true>), dim3(grid), dim3(gc::NT), 0,
+                           stream, a);
+    } else if (bm == 224) {
         if (NT_OK && peer_nt)
-            hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 7>), dim3(grid), dim3(gc::NT), 0, stream, a);
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 7, false>), dim3(grid), dim3(gc::NT), 0, stream, a);
         else
-            hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 7>), dim3(grid), dim3(gc::NT), 0, stream, a);
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 7, false>), dim3(grid), dim3(gc::NT), 0, stream, a);
     } else {
         if (NT_OK && peer_nt)
-            hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 8>), dim3(grid), dim3(gc::NT), 0, stream, a);
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 8, false>), dim3(grid), dim3(gc::NT), 0, stream, a);
         else
-            hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 8>), dim3(grid), dim3(gc::NT), 0, stream, a);
+            hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 8, false>), dim3(grid), dim3(gc::NT), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
 }

@@ -1,9 +1,11 @@
-"""Work split along K (stream-K): tiles shared by several workgroups must give
-exactly what whole tiles give on integer inputs (every partial sum exact in
-fp32), in all three modes, across shapes that exercise the split: fewer tiles
-than compute units, a tile shared by many workgroups, K-step counts that are
-not a multiple of the segment granularity, and back-to-back launches (the
-partial-ready flags carry a per-launch epoch and are never reset)."""
+"""Work split along K: tiles shared by several workgroups (each finishing its
+share of the tile from the others' partials) must give exactly what whole
+tiles give on integer inputs (every partial sum exact in fp32), in all three
+modes, across shapes that exercise the split: 2 to 16 chunks per tile, a last
+chunk shorter than the others, peer items starting at a per-tile step, shapes
+the host does not split (too few K-steps, peer items past the K loop), and
+back-to-back launches (the partial-ready flags carry a per-launch epoch and
+are never reset)."""
 import numpy as np
 import pytest
 import torch
@@ -33,15 +35,17 @@ def filled(shape):
 
 
 SHAPES = [
-    (300, 1040, 1024, 8),    # 10 tiles, 32 K-steps: tiles split over 4 workgroups
-    (64, 264, 4096, 4),      # 2 tiles, 128 K-steps: each tile over 16 workgroups
-    (513, 520, 896, 2),      # 28 K-steps (not a multiple of 8)
-    (1000, 776, 72, 8),      # 3 K-steps: every tile fits one workgroup's run
-    (4096, 1552, 512, 8),    # 112 tiles
-    (2304, 2560, 256, 4),    # 90 tiles
+    (300, 1040, 1024, 4),    # 10 tiles, 32 K-steps, 3 peers: 4 chunks of 8 steps
+    (64, 264, 4096, 4),      # 2 tiles, 128 K-steps: each tile in 16 chunks
+    (513, 520, 896, 2),      # 9 tiles, 28 K-steps: chunks of 8, 8, 8 and 4 steps
+    (4096, 1552, 512, 2),    # 112 tiles: 2 chunks each, 224 workgroups
+    (1000, 776, 72, 8),      # 3 K-steps: not split
+    (2304, 2560, 256, 4),    # 90 tiles, 8 K-steps: not split
+    (1000, 776, 1024, 8),    # 7 peers need 56 item steps, more than 32: not split
+    (256, 3648, 7168, 8),    # 15 tiles in 14 chunks of 16 steps, 7 peers: 22 phases
     # Tiles split into 3+ chunks start their peer items at a per-tile step:
-    (300, 1040, 4096, 4),    # 10 tiles, 128 K-steps, 3 peers: 14 phases
-    (200, 600, 2560, 8),     # 3 ragged tiles, 80 K-steps, 7 peers: 4 phases
+    (300, 1040, 4096, 4),    # 10 tiles, 16 chunks, 3 peers: 14 phases
+    (200, 600, 2560, 8),     # 3 ragged tiles, 10 chunks, 7 peers: 4 phases
 ]
 
 
