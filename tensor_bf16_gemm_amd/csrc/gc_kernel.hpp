@@ -51,9 +51,10 @@
 // accumulators while the K loop runs.  Item w = (peer w/8 - phase, row
 // block w%8) is the wave's 16 x 64 block of that peer; it is loaded into one
 // of two LDS slots of the wave at step w-2 and added at step w, so the peer
-// traffic streams behind the MFMA work.  The items of a tile take the 8 *
-// peers steps from step 8 * phase on (phase 0 but for tiles split into many
-// K chunks); items the K loop does not reach are added after it.
+// traffic streams behind the MFMA work.  The items of a whole tile take its
+// first 8 * peers steps (items the K loop does not reach are added after
+// it); in a tile split along K, each chunk takes its own share of the peers
+// at its first steps.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -87,10 +88,11 @@ struct Args {
     int N, K;
     int R, rank;
     int npeers;                // AR/RS: R-1
-    // Peer items of a tile start at step 8 * phase: phase 0 for a whole
-    // tile, tile % peer_phases for a split one (all its units agree).  The
-    // host keeps 8 * (peer_phases - 1 + npeers) <= KT.
-    int peer_phases;
+    // Peer items: a whole tile adds peer p's items at steps 8p .. 8p+7; a
+    // split unit of chunk c adds those of peers [ceil(c*npeers/sk_q),
+    // ceil((c+1)*npeers/sk_q)) at its first steps (the host keeps every
+    // chunk long enough for them), so the item loads are spread over the
+    // tile's units.
     int P, lo, hi;             // RS: slice height and owned valid rows [lo, hi)
     int m_rows;                // rows covered by tiles (per shard for AG)
     int tiles_m, tiles_n;      // per shard for AG
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
     int dp_lin = 0;                            // first tile of the next whole-tile round
     int unit = v;                              // next split unit of this workgroup
     for (;;) {
-        int L, g0, g1, phase;
+        int L, g0, g1, phase, peer_end = p.npeers;
         bool bad = false;
         if (!SPLIT && dp_lin < p.dp_tiles) {
             const int lin = dp_lin;
@@ -360,7 +362,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             g0 = c * p.sk_chunk;
             g1 = min(KT, g0 + p.sk_chunk);
             L = p.dp_tiles + (unit - c * p.sk_tiles);
-            phase = __builtin_amdgcn_readfirstlane(p.peer_phases > 1 ? L % p.peer_phases : 0);
+            // Peers [pa, pb) at steps g0 .. g0 + 8 (pb - pa) - 1: item w reads
+            // peer w/8 - phase.
+            const int pa = (c * p.npeers + p.sk_q - 1) / p.sk_q;
+            peer_end = __builtin_amdgcn_readfirstlane(((c + 1) * p.npeers + p.sk_q - 1) / p.sk_q);
+            phase = __builtin_amdgcn_readfirstlane(g0 / 8 - pa);
             unit += G;
         } else {
             break;
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int row_hi = MODE == MODE_RS ? p.hi : p.M;
         int W = 0;
         if (PEERS && m0 < row_hi && m0 + BMt > row_lo)
-            W = p.npeers * ITEMS_PER_GROUP;
+            W = peer_end * ITEMS_PER_GROUP;
         // chunk of instruction 0 is lane/16, of instruction 1 lane/16 + 4
         const int pd_n = n0 + wn * WN + 8 * (lane >> 4);
         const uint32_t pd_off = (uint32_t)(lane & 15) * N2 + (uint32_t)pd_n * 2u;

@@ -79,21 +79,31 @@ int64_t workspace_bytes_for(int groups)
 }
 
 // Chunk size (K-steps, a multiple of 8) for a problem of `tiles` < groups
-// tiles: the smallest that cuts each tile into at most min(16, groups /
-// tiles) chunks, so that the units fill as many workgroups as they can in
-// one round.  Every unit of a tile reads at most 1/q of each of the q - 1
-// other partials, so the hand-over costs about the same whatever q is, and
-// the shortest chunks win (measured at M = 256, N = 3648, K = 7168, 15
-// tiles: 14 chunks of 16 steps against 7 of 32).  Returns `kt` (no split)
-// when fewer than two chunks fit.
+// tiles, cut into q <= min(16, groups / tiles) chunks so that every unit has
+// a workgroup of its own.  Cost model in K-step units, fitted to
+// measurements at M=256 and 512, N=3648 and 6288, K=7168: a unit's K loop
+// takes its chunk, and every unit adds the traffic of handing its partial
+// over (about 0.5 MB through memory), worth 1/6 of a step each:
+// cost = chunk + units / 6.  Whole tiles cost kt + tiles / 6 on this scale.
+// (Measured at M=256, 15 tiles: 10 chunks of 24 steps 46.7 us, 7 of 32
+// 50.3 us, 14 of 16 50.5 us, 4 of 56 62.5 us.)  Returns `kt` for whole tiles.
 int pick_chunk(int kt, int tiles, int groups)
 {
     const int qmax = std::min(16, groups / tiles);
-    if (qmax < 2)
-        return kt;
-    int chunk = (kt + qmax - 1) / qmax;
-    chunk = (chunk + 7) / 8 * 8;
-    return chunk < kt ? chunk : kt;
+    int best = kt;
+    int64_t best_cost = 6 * (int64_t)kt + tiles;
+    for (int q = 2; q <= qmax; ++q) {
+        const int chunk = ((kt + q - 1) / q + 7) / 8 * 8;
+        if (chunk >= kt)
+            continue;
+        const int64_t units = (int64_t)((kt + chunk - 1) / chunk) * tiles;   // <= q * tiles
+        const int64_t cost = 6 * (int64_t)chunk + units;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = chunk;
+        }
+    }
+    return best;
 }
 
 template <int MODE>
@@ -128,12 +138,10 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     if (a.num_tiles == 0)
         return GC_OK;
     const int kt = (a.K + gc::BK - 1) / gc::BK;
-    // Peer items (AR, RS) take 8 * peers consecutive K-steps of a tile,
-    // from its first step on; for tiles split into three or more K chunks,
-    // from a per-tile multiple of 8 (measured: at M=512, 5 chunks of 48
-    // steps, 12 % faster; at M=1024, 2 chunks of 112, 5 % slower; whole
-    // tiles at M=4096, 10 % slower, when every tile shifts its items).
-    a.peer_phases = 1;
+    // Peer items (AR, RS) take 8 * peers consecutive K-steps of a whole
+    // tile, from its first step on (measured at M=4096: shifting them per
+    // tile was 10 % slower).  In a split tile each chunk takes its own peers
+    // at its first steps (see below).
     // Peer partials are read once.  When they are far larger than the
     // last-level cache, their loads are marked non-temporal so that they do
     // not evict the A and B tiles (measured at M=4096, 360 MB of peers: 3 %
@@ -153,7 +161,21 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     if (bm == 256 && peers->workspace && kt > 8 && a.num_tiles < cus && npeer_steps <= kt &&
         peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus)) {
         const int chunk = pick_chunk(kt, a.num_tiles, cus);
-        if (chunk < kt) {
+        const int q = (kt + chunk - 1) / chunk;
+        // Chunk c adds the items of peers [ceil(c*np/q), ceil((c+1)*np/q))
+        // at its first steps, so it must have 8 steps per peer.
+        bool items_fit = true;
+        for (int c = 0; c < q && chunk < kt; ++c) {
+            const int len = std::min(kt, (c + 1) * chunk) - c * chunk;
+            const int np = MODE == gc::MODE_AG
+                               ? 0
+                               : ((c + 1) * a.npeers + q - 1) / q - (c * a.npeers + q - 1) / q;
+            items_fit = items_fit && 8 * np <= len;
+        }
+        // One unit per workgroup: the workspace holds flags and a partial
+        // for at most `cus` units (pick_chunk keeps q * tiles <= cus).
+        const bool fits_ws = (int64_t)q * a.num_tiles <= cus;
+        if (chunk < kt && items_fit && fits_ws) {
             char *ws = (char *)peers->workspace;
             a.dp_tiles = 0;
             a.sk_tiles = a.num_tiles;
@@ -174,8 +196,6 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
             // their shares (they see its flag and claim within a few us)
             // before it claims what is left.
             a.sk_grace_spins = 32;
-            if (MODE != gc::MODE_AG && a.npeers > 0 && kt / 8 >= a.npeers && a.sk_q >= 3)
-                a.peer_phases = kt / 8 - a.npeers + 1;
             grid = a.sk_units;
         }
     }

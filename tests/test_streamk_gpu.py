@@ -2,10 +2,10 @@
 share of the tile from the others' partials) must give exactly what whole
 tiles give on integer inputs (every partial sum exact in fp32), in all three
 modes, across shapes that exercise the split: 2 to 16 chunks per tile, a last
-chunk shorter than the others, peer items starting at a per-tile step, shapes
-the host does not split (too few K-steps, peer items past the K loop), and
-back-to-back launches (the partial-ready flags carry a per-launch epoch and
-are never reset)."""
+chunk shorter than the others, chunks taking no, one or two peers' items,
+shapes the host does not split (too few K-steps, peer items past the K loop),
+and back-to-back launches (arrival counters, flags and claims carry a
+per-launch epoch and are never reset)."""
 import numpy as np
 import pytest
 import torch
@@ -38,14 +38,14 @@ SHAPES = [
     (300, 1040, 1024, 4),    # 10 tiles, 32 K-steps, 3 peers: 4 chunks of 8 steps
     (64, 264, 4096, 4),      # 2 tiles, 128 K-steps: each tile in 16 chunks
     (513, 520, 896, 2),      # 9 tiles, 28 K-steps: chunks of 8, 8, 8 and 4 steps
-    (4096, 1552, 512, 2),    # 112 tiles: 2 chunks each, 224 workgroups
+    (1024, 4096, 2048, 4),   # 64 tiles in 2 chunks of 32 steps, 3 peers: 2, 1
     (1000, 776, 72, 8),      # 3 K-steps: not split
     (2304, 2560, 256, 4),    # 90 tiles, 8 K-steps: not split
     (1000, 776, 1024, 8),    # 7 peers need 56 item steps, more than 32: not split
-    (256, 3648, 7168, 8),    # 15 tiles in 14 chunks of 16 steps, 7 peers: 22 phases
-    # Tiles split into 3+ chunks start their peer items at a per-tile step:
-    (300, 1040, 4096, 4),    # 10 tiles, 16 chunks, 3 peers: 14 phases
-    (200, 600, 2560, 8),     # 3 ragged tiles, 10 chunks, 7 peers: 4 phases
+    (256, 3648, 7168, 8),    # 15 tiles in 10 chunks of 24 steps, 7 peers: one each for 7
+    (512, 6400, 3072, 8),    # 50 tiles in 3 chunks of 32 steps, 7 peers: 3, 2, 2
+    (300, 1040, 4096, 4),    # 10 tiles in 8 chunks of 16 steps, 3 peers
+    (200, 600, 2560, 8),     # 3 ragged tiles, 10 chunks, 7 peers
 ]
 
 
