@@ -101,7 +101,7 @@ typedef struct gc_peers {
        (about one second). */
     uint32_t max_spins;
     /* All calls, optional: device workspace of at least
-       gemm_coll_workspace_bytes() bytes (about 128 MiB on MI355X),
+       gemm_coll_workspace_bytes() bytes (about 64 MiB on MI355X),
        zero-filled before its first use and not used by two calls at the
        same time.  With it, a problem with fewer 256 x 256 output tiles than
        compute units has its tiles split along K into chunks run by
