@@ -158,6 +158,69 @@ def ingest_counters(name: str, fetch_dir: str, write_dir: str, cal_fetch_dir: st
     return entry
 
 
+def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -> dict:
+    """The unfused pipeline on the same inputs, timed like the fused kernel:
+    a library GEMM (torch.matmul, hipBLASLt) writing the local product in
+    bf16, then the reduction kernel gemm_coll_peer_sum over the rows this
+    rank keeps (AR: all; RS and two-shot AR: its slice, the local product
+    being the published partial; two-shot AR also copies the slice into the
+    R-1 peer outputs).  AG: one GEMM on the concatenated shards."""
+    import torch
+    import tensor_bf16_gemm_amd as gc
+    dev = x["B"].device
+    B = x["B"]
+    copies = None
+    if w.mode == "ag":
+        a_in = x["shards"].reshape(w.R * w.M, w.K)
+        local = torch.empty((w.R * w.M, w.N), dtype=torch.bfloat16, device=dev)
+        reduce = None
+    else:
+        a_in = x["A"]
+        local = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        if w.mode == "ar":
+            out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+            reduce = lambda: gc.peer_sum(local, x["peers"], out)
+        else:
+            P = -(-w.M // w.R)
+            lo, hi = min(w.rank * P, w.M), min(w.rank * P + P, w.M)
+            out = torch.empty((hi - lo, w.N), dtype=torch.bfloat16, device=dev)
+            reduce = lambda: gc.peer_sum(local[lo:hi], x["peers"][:, lo:hi], out)
+            if w.mode == "ar2":
+                peer_out = torch.empty((w.R - 1, w.M, w.N), dtype=torch.bfloat16, device=dev)
+                copies = lambda: peer_out[:, lo:hi].copy_(out.unsqueeze(0).expand(w.R - 1, -1, -1))
+    gemm = lambda: torch.matmul(a_in, B, out=local)
+
+    def step():
+        gemm()
+        if reduce is not None:
+            reduce()
+        if copies is not None:
+            copies()
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        s0.record(st)
+        for _ in range(steps):
+            f()
+        s1.record(st)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / steps * 1e3
+
+    total = timed(step)
+    res = {"us_per_step": total, "gemm_us": timed(gemm),
+           "reduce_us": timed(reduce) if reduce is not None else 0.0,
+           "fused_speedup": total / fused_us,
+           "what": "torch.matmul (hipBLASLt) to a bf16 local product, then gemm_coll_peer_sum"
+                   + (" and the slice copies" if copies is not None else "")
+                   if w.mode != "ag" else "torch.matmul (hipBLASLt) on the concatenated shards",
+           "steps": steps}
+    return res
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the CPU oracle on leading rows of the workload (about target_s)."""
     import torch
@@ -224,6 +287,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the unfused baseline (library GEMM + peer-sum kernel)")
     ap.add_argument("--cold-launches", type=int, default=30,
                     help="launches timed one by one after a 512 MiB write that evicts the L2 "
                          "and last-level caches (0 = skip)")
@@ -349,6 +414,8 @@ def main(argv=None) -> int:
         "wall_s": wall,
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_unfused:
+        line["unfused_baseline"] = unfused_baseline(w, x, ms * 1e3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -53,11 +53,17 @@
  *                 or more, or a size above INT32_MAX)
  *     GC_EIO      the HIP launch failed
  *   M == 0 (or N == 0) is valid and launches nothing.
- * - K-split hand-over: the last workgroup to finish a split tile waits only
- *   for partners that have already finished their part of the K loop, so no
- *   call can deadlock.  If that wait still gives up (bounded), the tile is
- *   left unwritten and, when peers->status is not NULL, *status is set to
- *   GC_TIMEOUT_BASE + 16.
+ * - K-split hand-over: the workgroups sharing a split tile wait for one
+ *   another only a bounded time, and the last of them to finish its part of
+ *   the K loop completes whatever share of the tile the others did not
+ *   claim, so no call can deadlock whatever the order in which workgroups
+ *   get a compute unit.  If that last workgroup's own (guard) wait gives up,
+ *   the tile is left unwritten and, when peers->status is not NULL, *status
+ *   is set to GC_TIMEOUT_BASE + 16.
+ *
+ * gemm_coll_peer_sum is not a fused path: it is the reduction step of the
+ * unfused baseline (a library GEMM, then this kernel) that the fused entry
+ * points are measured against.
  */
 #ifndef GEMM_COLL_H
 #define GEMM_COLL_H
@@ -195,6 +201,23 @@ int64_t gemm_coll_workspace_bytes(void);
 
 /* Static description of a return code (never NULL). */
 const char *gemm_coll_strerror(int code);
+
+/* Unfused baseline, reduction step: out = bf16(local + the sum of npeers
+ * peer blocks), elementwise over rows x N, summed in fp32 in the order local,
+ * peer 0, ..., peer npeers-1 and rounded to nearest-even once.  After a
+ * library GEMM has written local = bf16(A.B), this is the unfused reference
+ * of "[Kimi-K3] Extend GEMM-RS to GEMM-AR" (test reference in 关键源码片段:
+ * the local matmul rounded to bf16, then the all-reduce) on one GPU.
+ *   local, out  [rows][N] dense; out may equal local, and must not overlap
+ *               the peer blocks otherwise.
+ *   partials    npeers blocks of [rows][N], block p starting p * peer_stride
+ *               elements after block 0 (a row slice [lo, hi) of [R-1][M][N]
+ *               partials: partials + lo*N with peer_stride = M*N).
+ * Pointers 16-byte aligned; peer_stride a multiple of 8, and >= rows*N when
+ * npeers > 1; 0 <= npeers <= 15.  GC_EINVAL otherwise, GC_EIO if the launch
+ * fails; rows*N == 0 launches nothing.  Enqueued on `stream`. */
+int gemm_coll_peer_sum(const gc_bf16 *local, const gc_bf16 *partials, int64_t rows, int64_t N,
+                       int npeers, int64_t peer_stride, gc_bf16 *out, void *stream);
 
 #ifdef __cplusplus
 }

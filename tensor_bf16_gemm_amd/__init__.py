@@ -20,7 +20,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "should_run", "strerror", "lib", "GcPeers",
+__all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "peer_sum", "should_run", "strerror",
+           "lib", "GcPeers",
            "workspace_bytes", "default_workspace",
            "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_TIMEOUT_BASE"]
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_coll_strerror.restype = ctypes.c_char_p
         L.gemm_coll_workspace_bytes.argtypes = []
         L.gemm_coll_workspace_bytes.restype = ctypes.c_int64
+        L.gemm_coll_peer_sum.argtypes = [vp, vp, i64, i64, ctypes.c_int, i64, vp, vp]
+        L.gemm_coll_peer_sum.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -243,3 +246,30 @@ def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: 
     _check(lib().ag_gemm(_ptr(A), _ptr(B), Ms, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "ag_gemm")
     return out
+
+
+def peer_sum(local, partials, out=None, *, stream=None):
+    """Reduction step of the unfused baseline: out [rows,N] = bf16(local +
+    sum over p of partials[p]), fp32 sum in the order local, peer 0, 1, ...
+    local: [rows,N] bf16, contiguous; partials: [npeers,rows,N] bf16 with
+    contiguous rows (stride(0) may be larger, e.g. a row slice of [R-1,M,N]
+    partials); out may be local."""
+    import torch
+    rows, N = local.shape
+    _bf16("local", local, (rows, N))
+    if not partials.is_cuda:
+        raise ValueError("partials must be a device tensor")
+    if partials.dtype != torch.bfloat16 or partials.dim() != 3 or tuple(partials.shape[1:]) != (rows, N):
+        raise ValueError(f"partials: expected bf16 [npeers, {rows}, {N}], got "
+                         f"{partials.dtype} {tuple(partials.shape)}")
+    if partials.shape[0] > 0 and rows * N > 0 and (partials.stride(2) != 1 or partials.stride(1) != N):
+        raise ValueError("partials: rows must be contiguous")
+    if out is None:
+        out = torch.empty((rows, N), dtype=torch.bfloat16, device=local.device)
+    _bf16("out", out, (rows, N))
+    npeers = partials.shape[0]
+    stride = partials.stride(0) if npeers > 0 else 0
+    _check(lib().gemm_coll_peer_sum(_ptr(local), _ptr(partials) if npeers else None, rows, N, npeers,
+                                    stride, _ptr(out), _stream(stream)), "gemm_coll_peer_sum")
+    return out
+

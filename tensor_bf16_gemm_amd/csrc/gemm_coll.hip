@@ -10,6 +10,7 @@
 
 #include "gc_kernel.hpp"
 #include "gemm_coll.h"
+#include "peer_sum.hpp"
 
 namespace {
 
@@ -219,6 +220,14 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
 }
 
+template <int NP>
+void launch_peer_sum(const uint16_t *local, const uint16_t *partials, int64_t stride, int64_t n,
+                     uint16_t *out, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gc::peer_sum_kernel<NP>), dim3(blocks), dim3(gc::PS_THREADS), 0, stream,
+                       local, partials, stride, n, out);
+}
+
 }  // namespace
 
 extern "C" {
@@ -364,6 +373,51 @@ int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K
     a.rank = rank;
     a.m_rows = (int)Ms;
     return dispatch<gc::MODE_AG>(a, peers, (hipStream_t)stream);
+}
+
+
+int gemm_coll_peer_sum(const gc_bf16 *local, const gc_bf16 *partials, int64_t rows, int64_t N,
+                       int npeers, int64_t peer_stride, gc_bf16 *out, void *stream)
+{
+    if (rows < 0 || N < 0 || npeers < 0 || npeers > 15)
+        return GC_EINVAL;
+    const int64_t n = rows * N;
+    if (n == 0)
+        return GC_OK;
+    if (!local || !out || !aligned16(local) || !aligned16(out))
+        return GC_EINVAL;
+    if (npeers > 0 && (!partials || !aligned16(partials) || peer_stride % 8 != 0 ||
+                       (npeers > 1 && peer_stride < n)))
+        return GC_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GC_EIO;
+    // enough workgroups for every CU several times over, each lane a few
+    // 16-byte vectors
+    const int64_t want = (n / 8 + gc::PS_THREADS - 1) / gc::PS_THREADS;
+    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)cu_count(dev) * 16));
+    const uint16_t *l = (const uint16_t *)local, *pp = (const uint16_t *)partials;
+    uint16_t *o = (uint16_t *)out;
+    hipStream_t st = (hipStream_t)stream;
+    switch (npeers) {
+    case 0: launch_peer_sum<0>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 1: launch_peer_sum<1>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 2: launch_peer_sum<2>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 3: launch_peer_sum<3>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 4: launch_peer_sum<4>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 5: launch_peer_sum<5>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 6: launch_peer_sum<6>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 7: launch_peer_sum<7>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 8: launch_peer_sum<8>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 9: launch_peer_sum<9>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 10: launch_peer_sum<10>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 11: launch_peer_sum<11>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 12: launch_peer_sum<12>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 13: launch_peer_sum<13>(l, pp, peer_stride, n, o, blocks, st); break;
+    case 14: launch_peer_sum<14>(l, pp, peer_stride, n, o, blocks, st); break;
+    default: launch_peer_sum<15>(l, pp, peer_stride, n, o, blocks, st); break;
+    }
+    return hipGetLastError() == hipSuccess ? GC_OK : GC_EIO;
 }
 
 }  // extern "C"

@@ -34,7 +34,8 @@ def header_functions():
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "gemm_coll_should_run",
-                          "gemm_coll_strerror", "gemm_coll_workspace_bytes"}, names
+                          "gemm_coll_strerror", "gemm_coll_workspace_bytes",
+                          "gemm_coll_peer_sum"}, names
     out = subprocess.run(["nm", "-D", "--defined-only", gc.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -131,3 +132,31 @@ def test_empty_problem_launches_nothing(L, name):
     # M == 0 or N == 0: valid, nothing to do, pointers may be NULL
     assert call(L, name, M=0, A=None, out=None, peers=False) == gc.GC_OK
     assert call(L, name, N=0, B=None, out=None, peers=False) == gc.GC_OK
+
+
+def psum(L, local=PA, partials=PA + 0x100000, rows=64, N=256, npeers=7, stride=64 * 256,
+         out=PA + 0x200000):
+    return L.gemm_coll_peer_sum(local, partials, rows, N, npeers, stride, out, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=-1), dict(N=-8), dict(npeers=-1), dict(npeers=16),
+    dict(local=None), dict(out=None), dict(partials=None),
+    dict(local=PA + 2), dict(out=PA + 0x200000 + 8), dict(partials=PA + 0x100000 + 4),
+    dict(stride=64 * 256 + 4),          # not a multiple of 8 elements
+    dict(stride=64 * 256 - 8),          # peer blocks would overlap
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_peer_sum_invalid_arguments(L, kw):
+    assert psum(L, **kw) == gc.GC_EINVAL
+
+
+def test_peer_sum_empty_and_no_peers(L):
+    # rows * N == 0: valid, nothing launched, pointers may be NULL
+    assert psum(L, rows=0, local=None, out=None, partials=None) == gc.GC_OK
+    assert psum(L, N=0, local=None, out=None, partials=None) == gc.GC_OK
+    # no peers: partials and stride are not looked at (still rejected: a bad
+    # local or out)
+    assert psum(L, npeers=0, partials=None, stride=3, local=PA + 2) == gc.GC_EINVAL
+    # a single peer block needs no stride
+    assert psum(L, npeers=1, stride=0, local=PA + 2) == gc.GC_EINVAL
+
