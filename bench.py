@@ -221,6 +221,74 @@ def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -
     return res
 
 
+def ag_arrival(w, x, resident_us: float, iters: int = 10, warmup: int = 3) -> dict:
+    """AG-GEMM with the shards arriving during the call: ag_push_shards copies
+    the other ranks' shards into a receive buffer through the DMA engines,
+    raising each flag after its shard, in ring order.  Timed three ways per
+    iteration (a fresh epoch each): the pushes alone; the pushes and then the
+    kernel on one stream; the kernel with the pushes on a side stream, which
+    it consumes as they land (streams joined between iterations, so the
+    receive buffer is never rewritten while it is read)."""
+    import torch
+    import tensor_bf16_gemm_amd as gc
+    dev = x["B"].device
+    R, rank = w.R, w.rank
+    recv = torch.zeros_like(x["shards"])
+    flags = torch.zeros(R, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((R * w.M, w.N), dtype=torch.bfloat16, device=dev)
+    n_ep = 3 * (iters + warmup) + 1
+    epochs = torch.arange(1, n_ep + 1, dtype=torch.int32, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ep = [0]
+
+    def push(stream):
+        e = ep[0]
+        gc.ag_push_shards(x["shards"], recv, flags, epochs[e:e + 1], R=R, rank=rank, stream=stream)
+
+    def kernel(stream):
+        gc.ag_gemm(x["A"], x["B"], recv, flags, status, out, R=R, rank=rank, epoch=ep[0] + 1,
+                   stream=stream)
+
+    def copy_only():
+        push(main)
+        ep[0] += 1
+
+    def serial():
+        push(main)
+        kernel(main)
+        ep[0] += 1
+
+    def overlapped():
+        side.wait_stream(main)
+        kernel(main)
+        push(side)
+        main.wait_stream(side)
+        ep[0] += 1
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(main)
+        for _ in range(iters):
+            f()
+        s1.record(main)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / iters * 1e3
+
+    copy_us = timed(copy_only)
+    res = {"copy_only_us": copy_us, "copy_then_gemm_us": timed(serial), "overlapped_us": timed(overlapped),
+           "resident_us": resident_us,
+           "copy_GBps": (R - 1) * w.M * w.K * 2 / (copy_us * 1e-6) / 1e9,
+           "status": int(status.item()),
+           "what": "ag_push_shards (DMA-engine copies + flag per shard, ring order) on a side stream "
+                   "while ag_gemm polls the flags, against copies then GEMM, and shards resident"}
+    return res
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the CPU oracle on leading rows of the workload (about target_s)."""
     import torch
@@ -287,6 +355,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-arrival", action="store_true",
+                    help="AG only: skip the run with shards arriving during the call")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the unfused baseline (library GEMM + peer-sum kernel)")
     ap.add_argument("--cold-launches", type=int, default=30,
@@ -416,6 +486,8 @@ def main(argv=None) -> int:
     }
     if not args.no_unfused:
         line["unfused_baseline"] = unfused_baseline(w, x, ms * 1e3)
+    if w.mode == "ag" and not args.no_arrival:
+        line["arrival"] = ag_arrival(w, x, ms * 1e3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)

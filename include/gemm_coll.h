@@ -22,6 +22,10 @@
  *             times B, with the shards consumed in ring order ("[Kimi-K3]
  *             AG-GEMM for Sequence Parallelism", Purpose and Implementation
  *             details).
+ *   ag_push_shards
+ *             the other ranks' side of AG-GEMM, emulated: DMA-engine copies
+ *             of their shards into ag_gemm's receive buffer, each followed
+ *             by its ready flag, in ring order (same page).
  *
  * The other ranks are represented by buffers in this GPU's memory (their
  * partial products, or their shards); nothing here moves data between GPUs.
@@ -201,6 +205,26 @@ int64_t gemm_coll_workspace_bytes(void);
 
 /* Static description of a return code (never NULL). */
 const char *gemm_coll_strerror(int code);
+
+/* AG-GEMM's producer side, emulated on one GPU: enqueues on `stream`, in
+ * ring order (round s = 1 .. R-1 brings shard q = (rank - s) mod R, the
+ * order in which ag_gemm consumes them), a copy of shard q from src into
+ * dst followed by a 4-byte copy of *epoch_word into flags[q], all through
+ * the DMA engines, so that they make progress while an ag_gemm launched on
+ * another stream holds every compute unit and polls those flags ("[Kimi-K3]
+ * AG-GEMM for Sequence Parallelism", Implementation details: the copy
+ * engine pushes one shard per round and then signals its receiver).  On one
+ * GPU the other ranks' shards are src; dst is ag_gemm's peers->shards.
+ *   src, dst    [R][Ms][K] bf16, 16-byte aligned, not overlapping; slot
+ *               `rank` of dst is neither read nor written.
+ *   flags       [R] uint32, 4-byte aligned (ag_gemm's peers->flags).
+ *   epoch_word  device pointer to the uint32 epoch to raise the flags to
+ *               (ag_gemm's peers->epoch), read by each flag copy.
+ * R and rank as for the other entry points.  GC_EINVAL for a NULL or
+ * misaligned pointer or R, rank or a size out of range; GC_EIO if a copy
+ * cannot be enqueued (earlier rounds may then already be enqueued). */
+int ag_push_shards(const gc_bf16 *src, gc_bf16 *dst, int64_t Ms, int64_t K, int R, int rank,
+                   uint32_t *flags, const uint32_t *epoch_word, void *stream);
 
 /* Unfused baseline, reduction step: out = bf16(local + the sum of npeers
  * peer blocks), elementwise over rows x N, summed in fp32 in the order local,

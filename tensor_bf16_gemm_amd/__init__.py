@@ -20,7 +20,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "peer_sum", "should_run", "strerror",
+__all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "ag_push_shards", "peer_sum",
+           "should_run", "strerror",
            "lib", "GcPeers",
            "workspace_bytes", "default_workspace",
            "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_TIMEOUT_BASE"]
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_coll_workspace_bytes.restype = ctypes.c_int64
         L.gemm_coll_peer_sum.argtypes = [vp, vp, i64, i64, ctypes.c_int, i64, vp, vp]
         L.gemm_coll_peer_sum.restype = ctypes.c_int
+        L.ag_push_shards.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.ag_push_shards.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -272,4 +275,22 @@ def peer_sum(local, partials, out=None, *, stream=None):
     _check(lib().gemm_coll_peer_sum(_ptr(local), _ptr(partials) if npeers else None, rows, N, npeers,
                                     stride, _ptr(out), _stream(stream)), "gemm_coll_peer_sum")
     return out
+
+
+def ag_push_shards(src, dst, flags, epoch_word, *, R: int, rank: int, stream=None):
+    """The other ranks' side of AG-GEMM, emulated: on `stream`, in ring order,
+    copy shard q of src [R,Ms,K] into dst [R,Ms,K] (ag_gemm's shards) and then
+    raise flags[q] to epoch_word[0], all through the DMA engines.  flags:
+    int32 [R] device tensor; epoch_word: int32 [1] device tensor."""
+    import torch
+    Rr, Ms, K = src.shape
+    if Rr != R:
+        raise ValueError(f"src has {Rr} shards, R={R}")
+    _bf16("src", src, (R, Ms, K))
+    _bf16("dst", dst, (R, Ms, K))
+    for name, t, n in (("flags", flags, R), ("epoch_word", epoch_word, 1)):
+        if t.dtype not in (torch.int32, torch.uint32) or tuple(t.shape) != (n,) or not t.is_cuda:
+            raise ValueError(f"{name}: expected a 32-bit device tensor of shape ({n},)")
+    _check(lib().ag_push_shards(_ptr(src), _ptr(dst), Ms, K, R, rank, _ptr(flags), _ptr(epoch_word),
+                                _stream(stream)), "ag_push_shards")
 

@@ -375,6 +375,32 @@ int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K
     return dispatch<gc::MODE_AG>(a, peers, (hipStream_t)stream);
 }
 
+int ag_push_shards(const gc_bf16 *src, gc_bf16 *dst, int64_t Ms, int64_t K, int R, int rank,
+                   uint32_t *flags, const uint32_t *epoch_word, void *stream)
+{
+    if (R < 2 || R > 16 || 128 % R != 0 || rank < 0 || rank >= R || Ms < 0 || K < 0)
+        return GC_EINVAL;
+    if (!src || !dst || !flags || !epoch_word || !aligned16(src) || !aligned16(dst) ||
+        ((uintptr_t)flags & 3u) || ((uintptr_t)epoch_word & 3u))
+        return GC_EINVAL;
+    const size_t shard = (size_t)Ms * (size_t)K;   // elements
+    hipStream_t st = (hipStream_t)stream;
+    // Round s brings shard q = (rank - s) mod R, the order ag_gemm consumes
+    // them in; the flag of a shard is written after its copy, in the same
+    // stream, so it is raised only once the shard has landed.  Both go
+    // through the DMA engines (no compute units), so they make progress
+    // while ag_gemm holds every compute unit.
+    for (int s = 1; s < R; ++s) {
+        const int q = (rank - s + R) % R;
+        if (shard > 0 && hipMemcpyAsync(dst + q * shard, src + q * shard, shard * 2,
+                                        hipMemcpyDeviceToDeviceNoCU, st) != hipSuccess)
+            return GC_EIO;
+        if (hipMemcpyAsync(flags + q, epoch_word, 4, hipMemcpyDeviceToDeviceNoCU, st) != hipSuccess)
+            return GC_EIO;
+    }
+    return GC_OK;
+}
+
 
 int gemm_coll_peer_sum(const gc_bf16 *local, const gc_bf16 *partials, int64_t rows, int64_t N,
                        int npeers, int64_t peer_stride, gc_bf16 *out, void *stream)

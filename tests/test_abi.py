@@ -35,7 +35,7 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "gemm_coll_should_run",
                           "gemm_coll_strerror", "gemm_coll_workspace_bytes",
-                          "gemm_coll_peer_sum"}, names
+                          "gemm_coll_peer_sum", "ag_push_shards"}, names
     out = subprocess.run(["nm", "-D", "--defined-only", gc.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -159,4 +159,19 @@ def test_peer_sum_empty_and_no_peers(L):
     assert psum(L, npeers=0, partials=None, stride=3, local=PA + 2) == gc.GC_EINVAL
     # a single peer block needs no stride
     assert psum(L, npeers=1, stride=0, local=PA + 2) == gc.GC_EINVAL
+
+
+def push(L, src=PA, dst=PA + 0x100000, Ms=64, K=256, R=8, rank=3, flags=PA + 0x200000,
+         epoch_word=PA + 0x200100):
+    return L.ag_push_shards(src, dst, Ms, K, R, rank, flags, epoch_word, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(R=1), dict(R=3), dict(R=32), dict(rank=8), dict(rank=-1), dict(Ms=-1), dict(K=-8),
+    dict(src=None), dict(dst=None), dict(flags=None), dict(epoch_word=None),
+    dict(src=PA + 8), dict(dst=PA + 0x100000 + 2), dict(flags=PA + 0x200002),
+    dict(epoch_word=PA + 0x200101),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_ag_push_invalid_arguments(L, kw):
+    assert push(L, **kw) == gc.GC_EINVAL
 
