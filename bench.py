@@ -289,6 +289,48 @@ def ag_arrival(w, x, resident_us: float, iters: int = 10, warmup: int = 3) -> di
     return res
 
 
+def sample_sclk(step, seconds: float = 1.0) -> dict | None:
+    """The shader clock while the step runs back to back: `rocm-smi
+    --showclocks`, run as a child process half-way through about `seconds`
+    of launches.  The chip is power-limited, so the clock under load is
+    below the 2.4 GHz of the peak figures.  None if the tool is missing."""
+    import re
+    import subprocess
+    import threading
+    import torch
+    res = {}
+
+    def probe():
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                               timeout=20)
+            lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l.lower()]
+            res["raw"] = lines[:2]
+            mhz = [int(m) for l in lines for m in re.findall(r"(\d+)\s*[Mm][Hh]z", l)]
+            res["sclk_mhz"] = mhz[-1] if mhz else None
+        except (OSError, subprocess.SubprocessError) as e:
+            res["error"] = str(e)
+
+    t = threading.Thread(target=probe)
+    t0 = time.perf_counter()
+    started = False
+    while time.perf_counter() - t0 < seconds or t.is_alive():
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+        if not started and time.perf_counter() - t0 > seconds / 2:
+            t.start()
+            started = True
+        if time.perf_counter() - t0 > 30:
+            break
+    if started:
+        t.join(timeout=30)
+    if "raw" not in res and "error" not in res:
+        return None
+    res["source"] = "rocm-smi --showclocks while the step runs back to back"
+    return res
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the CPU oracle on leading rows of the workload (about target_s)."""
     import torch
@@ -355,6 +397,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock under load (rocm-smi)")
     ap.add_argument("--no-arrival", action="store_true",
                     help="AG only: skip the run with shards arriving during the call")
     ap.add_argument("--no-unfused", action="store_true",
@@ -484,6 +528,8 @@ def main(argv=None) -> int:
         "wall_s": wall,
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_clock:
+        line["sclk"] = sample_sclk(step)
     if not args.no_unfused:
         line["unfused_baseline"] = unfused_baseline(w, x, ms * 1e3)
     if w.mode == "ag" and not args.no_arrival:
