@@ -526,9 +526,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // Item (peer pp, row block i) is the wave's 16 x 64 block of that
         // peer partial: rows blk .. blk+15 (blk = m0 + 128*wm + 16*i), columns
         // n0 + 64*wn .. +63.  It moves global -> LDS with two 16-byte DMA
-        // instructions per wave, stored chunk-major: 16-byte chunk c (columns
-        // 8c .. 8c+7) of block row r sits at (16*c + r) * 16, so lane l of
-        // instruction t fetches row l%16, chunk 4*t + l/16.  The buffer starts
+        // instructions per wave, instruction t reading whole 128-byte rows
+        // 8t .. 8t+7 of the block (rows cut into 64-byte pieces read about a
+        // third slower from HBM).  In LDS block row r takes 128 bytes at
+        // r * 128, its 16-byte chunk c (columns 8c .. 8c+7) at position
+        // c ^ ((r/2) % 8), so that a read-back pass over 16 rows hits 16
+        // distinct banks; the DMA writes in lane order, so lane l of
+        // instruction t fetches row r = 8t + l/8, chunk (l%8) ^ ((r/2) % 8)
+        // (for t = 1 that is instruction 0's chunk ^ 4).  The buffer starts
         // at the first row that may be read (>= row_lo) and ends at row_hi,
         // so rows outside [row_lo, row_hi) read as zero (rows below wrap past
         // 2^31); chunks past N are masked per lane on edge tiles.  Items
@@ -540,9 +545,9 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         int W = 0;
         if (PEERS && m0 < row_hi && m0 + BMt > row_lo)
             W = peer_end * ITEMS_PER_GROUP;
-        // chunk of instruction 0 is lane/16, of instruction 1 lane/16 + 4
-        const int pd_n = n0 + wn * WN + 8 * (lane >> 4);
-        const uint32_t pd_off = (uint32_t)(lane & 15) * N2 + (uint32_t)pd_n * 2u;
+        // row lane/8 and chunk (lane%8) ^ ((lane/16)%4) for instruction 0
+        const int pd_n = n0 + wn * WN + 8 * ((lane & 7) ^ ((lane >> 4) & 3));
+        const uint32_t pd_off = (uint32_t)(lane >> 3) * N2 + (uint32_t)pd_n * 2u;
         // Items this segment adds: those whose step lies in it (the drain
         // after the K loop moves the window to the items past KT).  The
         // phase shifts the tile's item steps; item w reads peer w/8 - phase
@@ -559,21 +564,28 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const u32x4_t rp = make_rsrc4(
                 pbase + (size_t)pp * p.M * p.N + (size_t)start * p.N, (uint32_t)rows * N2);
             const uint32_t off = pd_off - (uint32_t)(start - blk) * N2;
+            // instruction 1: rows 8 further on, chunk ^ 4 (32 columns back
+            // when the lane's chunk has bit 2 set, forward otherwise)
+            const bool back = (lane & 4) != 0;
+            const int pd_n1 = back ? pd_n - 32 : pd_n + 32;
+            const uint32_t off1 = off + 8u * N2 + (back ? (uint32_t)-64 : 64u);
             if constexpr (PEER_NT) {
                 dma16_nt(rp, ls, pd_n < p.N ? off : OOB);
-                dma16_nt(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
+                dma16_nt(rp, ls + 1024, pd_n1 < p.N ? off1 : OOB);
             } else {
                 dma16(rp, ls, pd_n < p.N ? off : OOB);
-                dma16(rp, ls + 1024, pd_n + 32 < p.N ? off + 64u : OOB);
+                dma16(rp, ls + 1024, pd_n1 < p.N ? off1 : OOB);
             }
         };
         auto peer_dma = [&](const uint8_t *slotbuf, int w, int i, uint32_t pd_off, int pd_n) {
             peer_dma_at(lds_addr(slotbuf) + (uint32_t)(wave * PSLOT), w, i, pd_off, pd_n);
         };
         // Reading back: lane (fi, fg) needs row fi, columns 16*j + 4*fg .. +3,
-        // i.e. half fg%2 of chunk 2*j + fg/2: byte j*512 + pc_off.  The 32
-        // lanes of one ds_read_b64 pass read 256 contiguous bytes.
-        const uint32_t pc_off = (uint32_t)(((fg >> 1) * 16 + fi) * 16 + 8 * (fg & 1));
+        // i.e. half fg%2 of chunk c = 2*j + fg/2, at position c ^ s of the
+        // row (s = (fi/2) % 8).  With s = 2*sh + sl that is byte
+        // pc_off ^ (32*j), pc_off = 128*fi + 8*(fg%2) + 16*((fg/2) ^ sl) + 32*sh.
+        const uint32_t pc_off = (uint32_t)(fi * 128 + 8 * (fg & 1) + 16 * ((fg >> 1) ^ ((fi >> 1) & 1)) +
+                                           32 * ((fi >> 2) & 3));
 
         f32x4_t acc[FMt][FN];
 #pragma unroll
@@ -663,7 +675,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                             const uint32_t pb = opaque(lds_addr(sl)) + wave * PSLOT;
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
-                                pv[j] = *lds_ptr<u32x2_t>(pb + pc_off + j * 512);
+                                pv[j] = *lds_ptr<u32x2_t>(pb + (pc_off ^ (uint32_t)(32 * j)));
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
                                 acc[u % FMt][j] += unpack_bf16x4(pv[j]);
@@ -871,11 +883,14 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             wait_vmcnt<0>();
         }
 
-        // ---- peer items the K loop did not reach: eight per round trip ----
+        // ---- peer items the K loop did not reach ----
         // (K shorter than the 8 * npeers item steps.)  The K loop is over, so
-        // each wave stages the up to 8 items of a row-block group in its
-        // 16 KiB of the idle LDS stages, once every wave's stage loads have
-        // landed and its stage reads are done.
+        // each wave streams them through its 16 KiB of the idle LDS stages,
+        // once every wave's stage loads have landed and its stage reads are
+        // done: half-groups of 4 items (row blocks 0-3 or 4-7 of a group of
+        // 8), the next half-group loading while one is added.  Every
+        // half-group issues the same 8 loads; items outside the window read
+        // an empty range, so they add zeros.
         // (A split launch has every item inside the K loop: the host splits
         // only when 8 * npeers <= KT.)
         if (!SPLIT && PEERS && W > KT) {
@@ -883,34 +898,52 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             barrier_only();
             wlo = KT;
             whi = W;
-            const int pd_n2 = n0 + wn * WN + 8 * (ln >> 4);
-            const uint32_t pd_off2 = (uint32_t)(ln & 15) * N2 + (uint32_t)pd_n2 * 2u;
-            const uint32_t pc_off2 = (uint32_t)(((fg2 >> 1) * 16 + fi2) * 16 + 8 * (fg2 & 1));
+            const int pd_n2 = n0 + wn * WN + 8 * ((ln & 7) ^ ((ln >> 4) & 3));
+            const uint32_t pd_off2 = (uint32_t)(ln >> 3) * N2 + (uint32_t)pd_n2 * 2u;
+            const uint32_t pc_off2 = (uint32_t)(fi2 * 128 + 8 * (fg2 & 1) +
+                                                16 * ((fg2 >> 1) ^ ((fi2 >> 1) & 1)) + 32 * ((fi2 >> 2) & 3));
             const uint8_t *wst = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1
                                : (wave >> 1) == 2 ? sS2 : sS3;
             const uint32_t reg = lds_addr(wst) + (uint32_t)((wave & 1) * 16384);
-            for (int w0 = KT & ~7; w0 < W; w0 += 8) {
+            const int g_first = KT & ~7;
+            const int nh = 2 * ((W - g_first + 7) / 8);   // half-groups, an even count
+            // half-group k: items g_first + 8 (k/2) + 4 (k%2) + r, row block
+            // 4 (k%2) + r, into slot 4 (k%2) + r
+            auto issue_half = [&](int k, int h) {
+                const int wb = g_first + 8 * (k >> 1) + 4 * h;
 #pragma unroll
-                for (int i = 0; i < FMt; ++i)
-                    if (w0 + i >= KT)
-                        peer_dma_at(reg + (uint32_t)(i * PSLOT), w0 + i, i, pd_off2, pd_n2);
-                wait_vmcnt<0>();
+                for (int r = 0; r < 4; ++r)
+                    peer_dma_at(reg + (uint32_t)((4 * h + r) * PSLOT), wb + r, 4 * h + r, pd_off2,
+                                pd_n2);
+            };
+            auto add_half = [&](int h) {
 #pragma unroll
-                for (int i = 0; i < FMt; ++i) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (w0 + i >= KT) {
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * h + r;
+                    if (i < FMt) {
                         u32x2_t pv[FN];
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
-                            pv[j] = *lds_ptr<u32x2_t>(reg + (uint32_t)(i * PSLOT) + pc_off2 +
-                                                      (uint32_t)(j * 512));
+                            pv[j] = *lds_ptr<u32x2_t>(reg + (uint32_t)(i * PSLOT) +
+                                                      (pc_off2 ^ (uint32_t)(32 * j)));
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
                             acc[i][j] += unpack_bf16x4(pv[j]);
                     }
                 }
-                wait_lgkmcnt0();      // reads done before the region refills
+                wait_lgkmcnt0();      // read back before the slots refill
+            };
+            issue_half(0, 0);
+            issue_half(1, 1);
+            for (int k = 0; k < nh; k += 2) {
+                wait_vmcnt<8>();      // half-group k landed (k+1 may be in flight)
+                add_half(0);
+                issue_half(k + 2, 0);
+                wait_vmcnt<8>();      // half-group k+1 landed
+                add_half(1);
+                issue_half(k + 3, 1);
             }
+            wait_vmcnt<0>();          // the two half-groups past the end
         }
 
         // ---- epilogue: bf16 stores, 8 bytes per lane per block ----
