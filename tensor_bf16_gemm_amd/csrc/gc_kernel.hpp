@@ -98,11 +98,12 @@ struct Args {
     int tiles_m, tiles_n;      // per shard for AG
     int num_tiles;             // total (AG: R * tiles_m * tiles_n)
     int group_m;               // row tiles per L2 group
-    // Work split.  A launch either takes dp_tiles whole tiles, round by
-    // round, or (dp_tiles == 0) cuts each of sk_tiles tiles along K into
-    // sk_q <= 16 chunks of sk_chunk steps (a multiple of 8; the last may be
-    // shorter), giving sk_units = sk_q * sk_tiles units numbered chunk-major
-    // (unit u is chunk u / sk_tiles of tile u % sk_tiles), one per workgroup:
+    // Work split.  A whole-tile launch takes tiles 0 .. dp_tiles-1, round by
+    // round.  A split launch cuts each of the sk_tiles tiles after them
+    // (tiles dp_tiles .. dp_tiles+sk_tiles-1) along K into sk_q <= 16 chunks
+    // of sk_chunk steps (a multiple of 8; the last may be shorter), giving
+    // sk_units = sk_q * sk_tiles units numbered chunk-major (unit u is
+    // chunk u / sk_tiles of tile dp_tiles + u % sk_tiles), one per workgroup:
     // the workgroups of one XCD run the same K range of neighbouring tiles.
     // The units of a tile exchange fp32 partials through sk_part[u] and
     // finish the tile in shares (see the kernel).  Counters, flags and
@@ -284,8 +285,9 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
 
 // PEER_NT: peer partials are loaded non-temporal (AR / RS).
 // FMT: row blocks of 16 per wave, 8 (256-row tiles) or 7 (224-row tiles).
-// SPLIT: the launch runs split units only (dp_tiles == 0); otherwise whole
-// tiles only, and the hand-over code is not compiled in.  (Each instance then
+// SPLIT: the launch runs split units only (after the dp_tiles whole tiles
+// that a launch before it took); otherwise whole tiles only, and the
+// hand-over code is not compiled in.  (Each instance then
 // gets a register allocation of its own: the hand-over's registers do not
 // weigh on the whole-tile K loop, nor the reverse.)
 template <int MODE, bool PEER_NT, int FMT, bool SPLIT>

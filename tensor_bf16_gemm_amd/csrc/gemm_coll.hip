@@ -107,6 +107,29 @@ int pick_chunk(int kt, int tiles, int groups)
     return best;
 }
 
+// Chunk size for splitting `rest` (< groups) tiles along K, or kt when they
+// are better run whole or cannot be split: every unit needs a workgroup of
+// its own, and chunk c, which adds the items of peers [ceil(c*np/q),
+// ceil((c+1)*np/q)) at its first steps, must have 8 steps per peer.
+int split_chunk(int kt, int64_t rest, int groups, int npeers)
+{
+    if (kt <= 8 || rest <= 0 || rest >= groups || 8 * npeers > kt)
+        return kt;
+    const int chunk = pick_chunk(kt, (int)rest, groups);
+    if (chunk >= kt)
+        return kt;
+    const int q = (kt + chunk - 1) / chunk;
+    if ((int64_t)q * rest > groups)
+        return kt;
+    for (int c = 0; c < q; ++c) {
+        const int len = std::min(kt, (c + 1) * chunk) - c * chunk;
+        const int np = ((c + 1) * npeers + q - 1) / q - (c * npeers + q - 1) / q;
+        if (8 * np > len)
+            return kt;
+    }
+    return chunk;
+}
+
 template <int MODE>
 int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
 {
@@ -119,17 +142,33 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     a.tiles_n = (a.N + gc::BN - 1) / gc::BN;
     const int64_t shards = MODE == gc::MODE_AG ? a.R : 1;
     auto tiles_for = [&](int64_t bm) { return (a.m_rows + bm - 1) / bm * a.tiles_n * shards; };
-    // Tile height: 256 rows, or 224 where the workgroups then get fewer
-    // rows of work, ceil(tiles / CUs) * height, by 3 % or more -- at M=4096,
-    // N=6288 on 256 CUs, 475 tiles of 224 rows fill two rounds where 400 of
-    // 256 rows also took two.  Only problems with a full round of tiles or
-    // more take 224 rows; smaller ones are split along K instead.
+    const int kt = (a.K + gc::BK - 1) / gc::BK;
+    const int item_peers = MODE == gc::MODE_AG ? 0 : a.npeers;
+    const bool ws_ok = peers->workspace != nullptr &&
+                       peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus);
+    // Tile height: 256 rows, or 224 where that is cheaper by 3 % or more,
+    // counted in rounds of 256-row tiles.  224-row tiles cost 7/8 of a round
+    // per round.  With 256-row tiles, a last partial round can be split
+    // along K (see below): about (chunk + 20 steps of hand-over) / kt of a
+    // round, else one more round.  At M=4096, N=6288 on 256 CUs, 475 tiles
+    // of 224 rows fill two rounds where 400 of 256 rows (144 left over, too
+    // many to split) also took two: 224.  At M=8448, N=2048, K=7168, 264
+    // tiles of 256 rows are a round plus 8 tiles split 14 ways: 256 rows,
+    // measured 248 us against 333 us with 224.  Only problems with a full
+    // round of tiles or more take 224 rows; smaller ones are split instead.
     const int64_t t256 = tiles_for(256), t224 = tiles_for(224);
     int bm = 256;
-    if (peers->tile_rows != 0)
+    if (peers->tile_rows != 0) {
         bm = (int)peers->tile_rows;
-    else if (t256 >= cus && (t224 + cus - 1) / cus * 224 * 100 < (t256 + cus - 1) / cus * 256 * 97)
-        bm = 224;
+    } else if (t256 >= cus) {
+        const int64_t r256 = t256 % cus;
+        const int ch = ws_ok ? split_chunk(kt, r256, cus, item_peers) : kt;
+        const double c256 = (double)(t256 / cus) +
+                            (r256 == 0 ? 0.0 : ch < kt ? (ch + 20.0) / kt : 1.0);
+        const double c224 = (double)((t224 + cus - 1) / cus) * (224.0 / 256.0);
+        if (c224 < 0.97 * c256)
+            bm = 224;
+    }
     const int64_t total = bm == 256 ? t256 : t224;
     if (total > INT32_MAX)
         return GC_ENOTSUP;
@@ -138,7 +177,6 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     a.group_m = 4;
     if (a.num_tiles == 0)
         return GC_OK;
-    const int kt = (a.K + gc::BK - 1) / gc::BK;
     // Peer items (AR, RS) take 8 * peers consecutive K-steps of a whole
     // tile, from its first step on (measured at M=4096: shifting them per
     // tile was 10 % slower).  In a split tile each chunk takes its own peers
@@ -153,36 +191,22 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     a.dp_tiles = a.num_tiles;
     a.sk_tiles = a.sk_q = a.sk_chunk = a.sk_units = 0;
     int grid = a.num_tiles < cus ? a.num_tiles : cus;
-    // Only problems with fewer tiles than workgroups are split along K:
-    // measured at M=4096 (400 tiles on 256 CUs), splitting the tiles of the
-    // last partial round, in any chunk size, was slower than running them
-    // whole.  A split launch needs every peer item inside the K loop
-    // (8 * npeers <= kt).
-    const int npeer_steps = MODE == gc::MODE_AG ? 0 : 8 * a.npeers;
-    if (bm == 256 && peers->workspace && kt > 8 && a.num_tiles < cus && npeer_steps <= kt &&
-        peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus)) {
-        const int chunk = pick_chunk(kt, a.num_tiles, cus);
-        const int q = (kt + chunk - 1) / chunk;
-        // Chunk c adds the items of peers [ceil(c*np/q), ceil((c+1)*np/q))
-        // at its first steps, so it must have 8 steps per peer.
-        bool items_fit = true;
-        for (int c = 0; c < q && chunk < kt; ++c) {
-            const int len = std::min(kt, (c + 1) * chunk) - c * chunk;
-            const int np = MODE == gc::MODE_AG
-                               ? 0
-                               : ((c + 1) * a.npeers + q - 1) / q - (c * a.npeers + q - 1) / q;
-            items_fit = items_fit && 8 * np <= len;
-        }
-        // One unit per workgroup: the workspace holds flags and a partial
-        // for at most `cus` units (pick_chunk keeps q * tiles <= cus).
-        const bool fits_ws = (int64_t)q * a.num_tiles <= cus;
-        if (chunk < kt && items_fit && fits_ws) {
+    // The tiles of the last partial round (all of them when there are fewer
+    // tiles than workgroups) may be split along K, when the cost model says
+    // that pays: then the full rounds run first as whole tiles, in a launch
+    // of their own, and the split launch takes the rest.  (At M=4096, 400
+    // tiles on 256 CUs, the 144 left over cannot take two chunks each, and
+    // splitting them into more units than CUs was measured slower.)
+    const int rest = a.num_tiles % cus;
+    if (bm == 256 && ws_ok && rest > 0) {
+        const int chunk = split_chunk(kt, rest, cus, item_peers);
+        if (chunk < kt) {
             char *ws = (char *)peers->workspace;
-            a.dp_tiles = 0;
-            a.sk_tiles = a.num_tiles;
+            a.dp_tiles = a.num_tiles - rest;
+            a.sk_tiles = rest;
             a.sk_chunk = chunk;
             a.sk_q = (kt + chunk - 1) / chunk;
-            a.sk_units = a.sk_q * a.num_tiles;
+            a.sk_units = a.sk_q * rest;
             a.sk_count = (unsigned long long *)ws;
             a.sk_claim = (uint32_t *)(ws + count_bytes(cus));
             a.sk_flags = (uint32_t *)(ws + count_bytes(cus) + claim_bytes(cus));
@@ -202,8 +226,20 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     }
     constexpr bool NT_OK = MODE != gc::MODE_AG;
     if (a.sk_units > 0) {
-        // Every tile is split (dp_tiles == 0), one unit per workgroup.  (The
-        // peer set of so few tiles is far below the non-temporal threshold.)
+        // The full rounds as whole tiles (256 rows), then the split launch:
+        // tiles dp_tiles .. num_tiles-1, one unit per workgroup.  (Stream
+        // order makes the second wait for the first.)
+        if (a.dp_tiles > 0) {
+            gc::Args d = a;
+            d.sk_units = 0;
+            if (NT_OK && peer_nt)
+                hipLaunchKernelGGL((gc::gc_kernel<MODE, NT_OK, 8, false>), dim3(cus), dim3(gc::NT), 0,
+                                   stream, d);
+            else
+                hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 8, false>), dim3(cus), dim3(gc::NT), 0,
+                                   stream, d);
+        }
+        // (the split tail reads few peers: plain loads)
         hipLaunchKernelGGL((gc::gc_kernel<MODE, false, 8, true>), dim3(grid), dim3(gc::NT), 0,
                            stream, a);
     } else if (bm == 224) {

@@ -159,3 +159,50 @@ def test_whole_tiles_partial_last_round(orc, mode, M, N, K, R):
         sh = host_bits(xc["shards"])
         assert_bits_equal(host_bits(out), orc.ag_gemm(sh[rank].copy(), Bh, sh, R, rank),
                           "AG whole tiles")
+
+
+@pytest.mark.parametrize("mode,M,N,K,R", [
+    ("ar", 8448, 2048, 4096, 4),   # 33 x 8 = 264 tiles: a full round, then 8 tiles in 8 chunks
+    ("rs", 8448, 2048, 4096, 4),   # the same; rank 3's slice reaches into the split tiles
+    ("ag", 1024, 2304, 4096, 8),   # 8 shards x 4 x 9 = 288 tiles: a full round, then 32 in 4 chunks
+])
+def test_tail_round_split_equals_whole(orc, mode, M, N, K, R):
+    """More tiles than CUs: the full rounds run as whole tiles and the tiles
+    of the last partial round are split along K in a second launch.  Bit-exact
+    against whole tiles on integer inputs, and sampled rows (the last ones,
+    in the split tiles, and some before) against the oracle."""
+    log(f"tail split {mode} M={M} N={N} K={K} R={R}")
+    rank = R - 1
+    xc = wl.integer_inputs(mode, M, N, K, R, rank=rank, seed=M + 3 * K)
+    x = to_dev(xc)
+    Bh = host_bits(xc["B"])
+    rows = np.r_[0:64, M // 2:M // 2 + 64, M - 320:M]
+    if mode == "ar":
+        whole = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=rank, workspace=False)
+        split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=rank)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_bits(split), host_bits(whole), "AR tail split vs whole")
+        Ah, Ph = host_bits(xc["A"]), host_bits(xc["peers"])
+        ref = orc.ar_rows(Ah[rows].copy(), Bh, Ph[:, rows].copy())
+        assert_bits_equal(host_bits(split)[rows], ref, "AR tail split vs oracle rows")
+    elif mode == "rs":
+        ws_w, ws_s = filled((M, N)), filled((M, N))
+        whole = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_w, R=R, rank=rank, workspace=False)
+        split = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_s, R=R, rank=rank)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_bits(split), host_bits(whole), "RS tail split vs whole")
+        assert_bits_equal(host_bits(ws_s), host_bits(ws_w), "RS tail split ws vs whole")
+    else:
+        flags = torch.ones(R, dtype=torch.int32, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        whole = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, R=R, rank=rank, epoch=1,
+                           workspace=False)
+        split = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, filled((R * M, N)), R=R,
+                           rank=rank, epoch=1)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert_bits_equal(host_bits(split), host_bits(whole), "AG tail split vs whole")
+        sh = host_bits(xc["shards"]).reshape(R * M, K)
+        arows = np.r_[0:64, R * M - 320:R * M]
+        ref = orc.ar_rows(sh[arows].copy(), Bh, None)
+        assert_bits_equal(host_bits(split)[arows], ref, "AG tail split vs oracle rows")
