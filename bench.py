@@ -290,45 +290,46 @@ def ag_arrival(w, x, resident_us: float, iters: int = 10, warmup: int = 3) -> di
 
 
 def sample_sclk(step, seconds: float = 1.0) -> dict | None:
-    """The shader clock while the step runs back to back: `rocm-smi
-    --showclocks`, run as a child process half-way through about `seconds`
-    of launches.  The chip is power-limited, so the clock under load is
-    below the 2.4 GHz of the peak figures.  None if the tool is missing."""
+    """The shader clock while the step runs back to back: the active level of
+    the driver's sysfs table pp_dpm_sclk (the line marked '*'), read half-way
+    through about `seconds` of launches.  (A file read: no other program is
+    started from this process.)  The chip is power-limited, so the clock
+    under load is below the 2.4 GHz of the peak figures.  None where the
+    file is not readable."""
+    import glob
     import re
-    import subprocess
-    import threading
     import torch
-    res = {}
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not files:
+        return None
 
-    def probe():
-        try:
-            r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
-                               timeout=20)
-            lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l.lower()]
-            res["raw"] = lines[:2]
-            mhz = [int(m) for l in lines for m in re.findall(r"(\d+)\s*[Mm][Hh]z", l)]
-            res["sclk_mhz"] = mhz[-1] if mhz else None
-        except (OSError, subprocess.SubprocessError) as e:
-            res["error"] = str(e)
+    def read():
+        out = []
+        for f in files:
+            try:
+                with open(f) as fh:
+                    for line in fh:
+                        if "*" in line:
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                out.append(int(m.group(1)))
+            except OSError:
+                pass
+        return out
 
-    t = threading.Thread(target=probe)
     t0 = time.perf_counter()
-    started = False
-    while time.perf_counter() - t0 < seconds or t.is_alive():
+    samples = []
+    while time.perf_counter() - t0 < seconds:
         for _ in range(8):
             step()
+        if time.perf_counter() - t0 > seconds / 2 and len(samples) < 8:
+            samples.append(read())      # launches queued ahead keep the GPU busy
         torch.cuda.synchronize()
-        if not started and time.perf_counter() - t0 > seconds / 2:
-            t.start()
-            started = True
-        if time.perf_counter() - t0 > 30:
-            break
-    if started:
-        t.join(timeout=30)
-    if "raw" not in res and "error" not in res:
+    vals = [v for s_ in samples for v in s_]
+    if not vals:
         return None
-    res["source"] = "rocm-smi --showclocks while the step runs back to back"
-    return res
+    return {"sclk_mhz": max(set(vals), key=vals.count), "samples": vals[:8],
+            "source": "active level of pp_dpm_sclk (sysfs) while the step runs back to back"}
 
 
 def cpu_baseline(w, x, target_s: float):
@@ -398,7 +399,7 @@ def main(argv=None) -> int:
                     help="target duration of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip sampling the shader clock under load (rocm-smi)")
+                    help="skip sampling the shader clock under load (sysfs pp_dpm_sclk)")
     ap.add_argument("--no-arrival", action="store_true",
                     help="AG only: skip the run with shards arriving during the call")
     ap.add_argument("--no-unfused", action="store_true",
