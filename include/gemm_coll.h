@@ -63,7 +63,9 @@
  *   claim, so no call can deadlock whatever the order in which workgroups
  *   get a compute unit.  If that last workgroup's own (guard) wait gives up,
  *   the tile is left unwritten and, when peers->status is not NULL, *status
- *   is set to GC_TIMEOUT_BASE + 16.
+ *   is set to GC_TIMEOUT_BASE + 16.  (For tests, the environment variable
+ *   GEMM_COLL_SPLIT_WAIT_SPINS, read at each call, overrides how long the
+ *   other workgroups wait before leaving their share to the last one.)
  *
  * gemm_coll_peer_sum is not a fused path: it is the reduction step of the
  * unfused baseline (a library GEMM, then this kernel) that the fused entry

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
@@ -217,6 +218,11 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
             // units' arrival times when they run at once (measured: up to
             // 25 us), short when they do not.
             a.sk_wait_spins = 256;
+            // Test hook: GEMM_COLL_SPLIT_WAIT_SPINS overrides that limit (a
+            // limit of 1 makes nearly every unit give up at once, so that
+            // the last unit to arrive finishes their shares).
+            if (const char *e = getenv("GEMM_COLL_SPLIT_WAIT_SPINS"))
+                a.sk_wait_spins = (uint32_t)std::max(1L, strtol(e, nullptr, 10));
             // The last unit to arrive leaves the others about 30 us to claim
             // their shares (they see its flag and claim within a few us)
             // before it claims what is left.

@@ -206,3 +206,47 @@ def test_tail_round_split_equals_whole(orc, mode, M, N, K, R):
         arows = np.r_[0:64, R * M - 320:R * M]
         ref = orc.ar_rows(sh[arows].copy(), Bh, None)
         assert_bits_equal(host_bits(split)[arows], ref, "AG tail split vs oracle rows")
+
+
+@pytest.mark.parametrize("mode,M,N,K,R", [
+    ("ar", 256, 3648, 7168, 8),    # 15 tiles, 10 chunks each
+    ("rs", 300, 1040, 4096, 4),    # 10 tiles, 8 chunks each
+    ("ag", 100, 520, 1024, 4),     # 12 tiles, 4 chunks each
+])
+def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R):
+    """The split hand-over's fallback, forced from the host: with the units'
+    wait limited to one poll, nearly every unit that is not the last to
+    arrive leaves its share, and the last one finishes it.  The result must
+    not change (bit-exact on integer inputs)."""
+    log(f"split units giving up: {mode} M={M} N={N} K={K} R={R}")
+    rank = 1
+    xc = wl.integer_inputs(mode, M, N, K, R, rank=rank, seed=M + 7 * K)
+    x = to_dev(xc)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    monkeypatch.setenv("GEMM_COLL_SPLIT_WAIT_SPINS", "1")
+    if mode == "ar":
+        split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=rank, status=status)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
+        whole = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=rank, workspace=False)
+    elif mode == "rs":
+        ws_s = filled((M, N))
+        split = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_s, R=R, rank=rank, status=status)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
+        ws_w = filled((M, N))
+        whole = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_w, R=R, rank=rank, workspace=False)
+        torch.cuda.synchronize()
+        assert_bits_equal(host_bits(ws_s), host_bits(ws_w), "RS ws, units giving up")
+    else:
+        flags = torch.ones(R, dtype=torch.int32, device=DEV)
+        split = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, filled((R * M, N)), R=R,
+                           rank=rank, epoch=1)
+        torch.cuda.synchronize()
+        monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
+        st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+        whole = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, st2, R=R, rank=rank, epoch=1,
+                           workspace=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert_bits_equal(host_bits(split), host_bits(whole), f"{mode} split with units giving up")
