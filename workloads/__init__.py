@@ -69,6 +69,10 @@ WORKLOADS: dict[str, Workload] = {
                  "KDA projection M=4096, GEMM-AR (headline)"),
         Workload("kda4096_ar2", "ar2", 4096, 6288, 7168, 8, 0, 1.0, _isqrt(7168), 1.0, 0,
                  "KDA projection M=4096, GEMM-AR by the two-shot flow (rank 0's share)"),
+        Workload("kda64_ar", "ar", 64, 6288, 7168, 8, 0, 1.0, _isqrt(7168), 1.0, 0,
+                 "KDA decode size M=64, below the dispatch gate: GEMM-AR, tiles split along K"),
+        Workload("kda16_ar", "ar", 16, 6288, 7168, 8, 0, 1.0, _isqrt(7168), 1.0, 0,
+                 "KDA decode size M=16, below the dispatch gate: GEMM-AR, tiles split along K"),
         Workload("kda4096_k0", "ar", 4096, 6288, 0, 8, 0, 1.0, 1.0, 1.0, 0,
                  "KDA M=4096 with K=0: the fused kernel reduces to the peer sum (epilogue bandwidth)"),
         Workload("ag_kda", "ag", 4096, 6288, 7168, 8, 3, 1.0, _isqrt(7168), 1.0, 0,
