@@ -123,8 +123,9 @@ typedef struct gc_peers {
     void *workspace;
     uint64_t workspace_bytes;
     /* All calls, optional: output tile height in rows, 0 = chosen per
-       problem (256, or 224 where that gives the workgroups less work),
-       256 or 224 = forced; any other value is GC_EINVAL.  Results agree to
+       problem (64 for at most 64 rows per shard, 128 for at most 128, else
+       256, or 224 where that gives the workgroups less work); 64, 128, 224
+       or 256 = forced; any other value is GC_EINVAL.  Results agree to
        rounding of the fp32 sums (the peer partials are added at different
        K-steps).  224-row tiles are never split along K. */
     uint32_t tile_rows;
@@ -200,6 +201,36 @@ int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K
  * their unfused GEMM there.  The entry points themselves run any M >= 0.
  */
 int gemm_coll_should_run(int64_t M);
+
+/* Launch plan that a call with these arguments makes (host arithmetic only:
+ * no device is touched, so it also runs without a GPU), for tests and for
+ * callers that want to see the tiling.  `mode` is GC_MODE_AR, GC_MODE_RS
+ * (also gemm_ar_two_shot) or GC_MODE_AG (M is then Ms, the shard rows);
+ * `cus` the device's compute units (256 on MI355X); `with_workspace` whether
+ * the call passes a large enough gc_peers.workspace; `tile_rows` as in
+ * gc_peers.  Tiles are numbered shard-major (AG), then in groups of row
+ * tiles; the first whole_tiles run whole, the split_tiles after them are cut
+ * along K into `chunks` chunks of chunk_steps K-steps of 32 (the last chunk
+ * may be shorter), one workgroup per (chunk, tile) unit.  GC_EINVAL for
+ * arguments the entry points would refuse (and for `plan` NULL, `mode` out
+ * of range or `cus` outside 1 .. 4096), GC_ENOTSUP likewise; M or N == 0
+ * gives an empty plan (tiles 0). */
+#define GC_MODE_AR 0
+#define GC_MODE_RS 1
+#define GC_MODE_AG 2
+typedef struct gc_plan {
+    uint32_t tile_rows;   /* 64, 128, 224 or 256 */
+    int32_t tiles;        /* output tiles (over all shards for AG) */
+    int32_t whole_tiles;  /* tiles computed whole, in rounds of `grid` */
+    int32_t split_tiles;  /* tiles split along K after them (0: none) */
+    int32_t chunks;       /* K chunks per split tile (0: none) */
+    int32_t chunk_steps;  /* K-steps per chunk, a multiple of 8 (0: none) */
+    int32_t units;        /* split_tiles * chunks, one workgroup each */
+    int32_t grid;         /* workgroups of the last launch */
+    int32_t peer_nt;      /* peer partials loaded non-temporal */
+} gc_plan;
+int gemm_coll_plan(int mode, int64_t M, int64_t N, int64_t K, int R, int rank, int cus,
+                   int with_workspace, uint32_t tile_rows, gc_plan *plan);
 
 /* Bytes of workspace that lets a call split tiles along K on the current
  * device (see gc_peers.workspace); negative on a HIP error. */

@@ -21,8 +21,8 @@ import ctypes
 import os
 
 __all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "ag_push_shards", "peer_sum",
-           "should_run", "strerror",
-           "lib", "GcPeers",
+           "should_run", "strerror", "plan",
+           "lib", "GcPeers", "GcPlan",
            "workspace_bytes", "default_workspace",
            "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_TIMEOUT_BASE"]
 
@@ -52,6 +52,23 @@ class GcPeers(ctypes.Structure):
     ]
 
 
+class GcPlan(ctypes.Structure):
+    """Mirror of ``gc_plan`` in include/gemm_coll.h."""
+    _fields_ = [
+        ("tile_rows", ctypes.c_uint32),
+        ("tiles", ctypes.c_int32),
+        ("whole_tiles", ctypes.c_int32),
+        ("split_tiles", ctypes.c_int32),
+        ("chunks", ctypes.c_int32),
+        ("chunk_steps", ctypes.c_int32),
+        ("units", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("peer_nt", ctypes.c_int32),
+    ]
+
+
+MODES = {"ar": 0, "rs": 1, "ag": 2}
+
 _lib = None
 
 
@@ -79,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.gemm_coll_peer_sum.restype = ctypes.c_int
         L.ag_push_shards.argtypes = [vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.ag_push_shards.restype = ctypes.c_int
+        L.gemm_coll_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                     ctypes.POINTER(GcPlan)]
+        L.gemm_coll_plan.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -90,6 +111,18 @@ def strerror(code: int) -> str:
 def should_run(M: int) -> bool:
     """Dispatch gate: True when the fused path should serve M tokens (M >= 128)."""
     return bool(lib().gemm_coll_should_run(int(M)))
+
+
+def plan(mode: str, M: int, N: int, K: int, R: int, rank: int = 0, *, cus: int = 256,
+         workspace: bool = True, tile_rows: int = 0) -> dict:
+    """The launch plan a call would make (``gemm_coll_plan``; no GPU needed).
+    ``mode`` is "ar", "rs" (also the two-shot AR) or "ag" (M = shard rows)."""
+    out = GcPlan()
+    rc = lib().gemm_coll_plan(MODES[mode], int(M), int(N), int(K), int(R), int(rank), int(cus),
+                              int(bool(workspace)), int(tile_rows), ctypes.byref(out))
+    if rc != GC_OK:
+        raise RuntimeError(f"gemm_coll_plan failed: {strerror(rc)} ({rc})")
+    return {name: int(getattr(out, name)) for name, _ in GcPlan._fields_}
 
 
 _workspaces: dict = {}

@@ -293,9 +293,10 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
 template <int MODE, bool PEER_NT, int FMT, bool SPLIT>
 __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
-    static_assert(FMT == 8 || FMT == 7, "row blocks per wave");
-    static_assert(!SPLIT || FMT == 8, "224-row tiles are never split");
+    static_assert(FMT == 8 || FMT == 7 || FMT == 4 || FMT == 2, "row blocks per wave");
+    static_assert(!SPLIT || FMT != 7, "224-row tiles are never split");
     constexpr int FMt = FMT, WMt = 16 * FMT, BMt = 2 * WMt;
+    constexpr int NSEG = 2 * FMt;          // hand-over segments per wave
     // One array per operand and stage: distinct LDS objects carry distinct
     // alias scopes, so the compiler knows that the loads filling one stage
     // cannot alias the fragment reads of another and does not wait for them.
@@ -703,9 +704,10 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int pn_base2 = n0 + wn * WN + 4 * fg2;
 
         // ---- split tile: exchange partials, finish the tile in shares ----
-        // Each wave's 32 accumulator blocks form 16 segments, row block i and
-        // column half h (blocks (i, 2h) and (i, 2h+1)); share k of a tile's q
-        // units is segments [16k/q, 16(k+1)/q).  Every unit stores its whole
+        // Each wave's 4*FMt accumulator blocks form NSEG = 2*FMt segments,
+        // row block i and column half h (blocks (i, 2h) and (i, 2h+1)); share
+        // k of a tile's q units is segments [NSEG*k/q, NSEG*(k+1)/q) (empty
+        // for some k when q > NSEG).  Every unit stores its whole
         // fp32 partial, raises its flag and counts itself in on the tile's
         // arrival counter.  A unit that is not the last to arrive waits a
         // short, bounded time for the other units' flags; if they all come,
@@ -729,12 +731,12 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const int stt = u - sc * p.sk_tiles;
             const int nq = p.sk_q;
             const uint32_t lane16 = (uint32_t)ln * 16u;
-            const uint32_t wave_off = (uint32_t)(wave * FM * FN * 1024);
+            const uint32_t wave_off = (uint32_t)(wave * FMt * FN * 1024);
             if (!bad) {
                 const __amdgpu_buffer_rsrc_t rp =
                     make_rsrc(p.sk_part + (size_t)u * PART_FLOATS, PART_FLOATS * 4u);
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FMt; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(
@@ -827,7 +829,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 uint32_t m = 0;
                 for (int k = 0; k < nq; ++k)
                     if ((won >> k) & 1u)
-                        m |= (1u << (16 * (k + 1) / nq)) - (1u << (16 * k / nq));
+                        m |= (1u << (NSEG * (k + 1) / nq)) - (1u << (NSEG * k / nq));
                 if (lane == 0)
                     *cell = (int)m;
             }
@@ -875,7 +877,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 wait_lgkmcnt0();
                 const int sg = seg_of(t % ns);
 #pragma unroll
-                for (int s2 = 0; s2 < 2 * FM; ++s2)
+                for (int s2 = 0; s2 < NSEG; ++s2)
                     if (sg == s2) {
                         acc[s2 >> 1][2 * (s2 & 1)] += __builtin_bit_cast(f32x4_t, x0);
                         acc[s2 >> 1][2 * (s2 & 1) + 1] += __builtin_bit_cast(f32x4_t, x1);

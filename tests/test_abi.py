@@ -35,7 +35,7 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "gemm_coll_should_run",
                           "gemm_coll_strerror", "gemm_coll_workspace_bytes",
-                          "gemm_coll_peer_sum", "ag_push_shards"}, names
+                          "gemm_coll_peer_sum", "ag_push_shards", "gemm_coll_plan"}, names
     out = subprocess.run(["nm", "-D", "--defined-only", gc.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
@@ -65,6 +65,23 @@ def test_peers_struct_layout(tmp_path):
     py_vals = [P.partials.offset, P.ws.offset, P.shards.offset, P.flags.offset, P.epoch.offset,
                P.status.offset, P.max_spins.offset, ctypes.sizeof(P), P.workspace.offset,
                P.workspace_bytes.offset, P.tile_rows.offset, P.peer_out.offset]
+    assert c_vals == py_vals
+
+
+def test_plan_struct_layout(tmp_path):
+    """ctypes' GcPlan must match the C struct gc_plan (offsets and size)."""
+    names = [n for n, _ in gc.GcPlan._fields_]
+    src = tmp_path / "plan.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "gemm_coll.h"\n'
+        "int main(void){" + "".join(f'printf("%zu ", offsetof(gc_plan,{n}));' for n in names) +
+        'printf("%zu\\n", sizeof(gc_plan)); return 0;}\n')
+    exe = tmp_path / "plan"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
+                    str(src)], check=True)
+    c_vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                             check=True).stdout.split()]
+    py_vals = [getattr(gc.GcPlan, n).offset for n in names] + [ctypes.sizeof(gc.GcPlan)]
     assert c_vals == py_vals
 
 
@@ -102,7 +119,7 @@ ALL = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"]
     dict(M=-1), dict(N=-8), dict(K=-8), dict(N=12), dict(K=20),
     dict(out=None), dict(A=None), dict(B=None), dict(peers=False),
     dict(A=PA + 8), dict(B=PA + 0x100000 + 2), dict(out=PA + 0x200000 + 4),
-    dict(tile_rows=128), dict(tile_rows=1),
+    dict(tile_rows=96), dict(tile_rows=1),
 ], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
 def test_invalid_arguments(L, name, kw):
     assert call(L, name, **kw) == gc.GC_EINVAL

@@ -5,7 +5,10 @@ modes, across shapes that exercise the split: 2 to 16 chunks per tile, a last
 chunk shorter than the others, chunks taking no, one or two peers' items,
 shapes the host does not split (too few K-steps, peer items past the K loop),
 and back-to-back launches (arrival counters, flags and claims carry a
-per-launch epoch and are never reset)."""
+per-launch epoch and are never reset).  The split tests run with 256-row tiles
+(tile_rows=256) and with the host's own choice, which takes 64- or 128-row
+tiles for most of these shapes (4 or 8 hand-over segments per wave instead of
+16)."""
 import numpy as np
 import pytest
 import torch
@@ -34,6 +37,7 @@ def filled(shape):
     return torch.full(shape, SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
 
 
+# Comments: the plan with 256-row tiles.
 SHAPES = [
     (300, 1040, 1024, 4),    # 10 tiles, 32 K-steps, 3 peers: 4 chunks of 8 steps
     (64, 264, 4096, 4),      # 2 tiles, 128 K-steps: each tile in 16 chunks
@@ -49,14 +53,16 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("rows", [256, 0])
 @pytest.mark.parametrize("M,N,K,R", SHAPES)
-def test_ar_split_equals_whole(orc, M, N, K, R):
-    log(f"stream-K AR M={M} N={N} K={K} R={R}")
+def test_ar_split_equals_whole(orc, M, N, K, R, rows):
+    log(f"stream-K AR M={M} N={N} K={K} R={R} tile_rows={rows}")
     xc = wl.integer_inputs("ar", M, N, K, R, seed=M + N + K)
     x = to_dev(xc)
     whole = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=1, workspace=False)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=1, status=status)
+    split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=1, status=status,
+                       tile_rows=rows)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert_bits_equal(host_bits(split), host_bits(whole), "split vs whole")
@@ -64,15 +70,16 @@ def test_ar_split_equals_whole(orc, M, N, K, R):
                                                     host_bits(xc["peers"]), R), "split vs oracle")
 
 
+@pytest.mark.parametrize("rows", [256, 0])
 @pytest.mark.parametrize("M,N,K,R", SHAPES[:3] + SHAPES[-2:])
-def test_rs_split_all_ranks(orc, M, N, K, R):
-    log(f"stream-K RS M={M} N={N} K={K} R={R}")
+def test_rs_split_all_ranks(orc, M, N, K, R, rows):
+    log(f"stream-K RS M={M} N={N} K={K} R={R} tile_rows={rows}")
     xc = wl.integer_inputs("rs", M, N, K, R, seed=M + 2 * K)
     x = to_dev(xc)
     A, B, peers = (host_bits(xc[k]) for k in ("A", "B", "peers"))
     for rank in range(R):
         ws = filled((M, N))
-        out = gc.gemm_rs(x["A"], x["B"], x["peers"], ws, R=R, rank=rank)
+        out = gc.gemm_rs(x["A"], x["B"], x["peers"], ws, R=R, rank=rank, tile_rows=rows)
         torch.cuda.synchronize()
         ws_ref = np.full((M, N), SENTINEL, np.uint16)
         ref, ws_ref = orc.gemm_rs(A, B, peers, R, rank, ws_ref)
@@ -80,15 +87,17 @@ def test_rs_split_all_ranks(orc, M, N, K, R):
         assert_bits_equal(host_bits(ws), ws_ref, f"RS split ws rank {rank}")
 
 
+@pytest.mark.parametrize("rows", [256, 0])
 @pytest.mark.parametrize("Ms,N,K,R", [(100, 520, 1024, 4), (512, 1040, 896, 8)])
-def test_ag_split(orc, Ms, N, K, R):
-    log(f"stream-K AG Ms={Ms} N={N} K={K} R={R}")
+def test_ag_split(orc, Ms, N, K, R, rows):
+    log(f"stream-K AG Ms={Ms} N={N} K={K} R={R} tile_rows={rows}")
     rank = R - 1
     xc = wl.integer_inputs("ag", Ms, N, K, R, rank=rank, seed=Ms + K)
     x = to_dev(xc)
     flags = torch.ones(R, dtype=torch.int32, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    out = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, R=R, rank=rank, epoch=1)
+    out = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, R=R, rank=rank, epoch=1,
+                     tile_rows=rows)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     sh = host_bits(xc["shards"])
@@ -208,12 +217,13 @@ def test_tail_round_split_equals_whole(orc, mode, M, N, K, R):
         assert_bits_equal(host_bits(split)[arows], ref, "AG tail split vs oracle rows")
 
 
+@pytest.mark.parametrize("rows", [256, 0])
 @pytest.mark.parametrize("mode,M,N,K,R", [
-    ("ar", 256, 3648, 7168, 8),    # 15 tiles, 10 chunks each
-    ("rs", 300, 1040, 4096, 4),    # 10 tiles, 8 chunks each
-    ("ag", 100, 520, 1024, 4),     # 12 tiles, 4 chunks each
+    ("ar", 256, 3648, 7168, 8),    # 15 tiles, 10 chunks each (128 rows: 30 tiles, 7 chunks)
+    ("rs", 300, 1040, 4096, 4),    # 10 tiles, 8 chunks each (64 rows: 25 tiles, 8 chunks)
+    ("ag", 100, 520, 1024, 4),     # 12 tiles, 4 chunks each (64 rows: 24 tiles, 4 chunks)
 ])
-def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R):
+def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R, rows):
     """The split hand-over's fallback, forced from the host: with the units'
     wait limited to one poll, nearly every unit that is not the last to
     arrive leaves its share, and the last one finishes it.  The result must
@@ -225,13 +235,15 @@ def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R):
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     monkeypatch.setenv("GEMM_COLL_SPLIT_WAIT_SPINS", "1")
     if mode == "ar":
-        split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=rank, status=status)
+        split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=rank, status=status,
+                           tile_rows=rows)
         torch.cuda.synchronize()
         monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
         whole = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=rank, workspace=False)
     elif mode == "rs":
         ws_s = filled((M, N))
-        split = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_s, R=R, rank=rank, status=status)
+        split = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_s, R=R, rank=rank, status=status,
+                           tile_rows=rows)
         torch.cuda.synchronize()
         monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
         ws_w = filled((M, N))
@@ -241,7 +253,7 @@ def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R):
     else:
         flags = torch.ones(R, dtype=torch.int32, device=DEV)
         split = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, filled((R * M, N)), R=R,
-                           rank=rank, epoch=1)
+                           rank=rank, epoch=1, tile_rows=rows)
         torch.cuda.synchronize()
         monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
         st2 = torch.zeros(1, dtype=torch.int32, device=DEV)

@@ -101,9 +101,9 @@ def test_auto_choice_matches_256_float(orc):
 
 
 def test_tile_rows_rejected():
-    """Heights other than 0, 224 and 256 are refused before any launch."""
+    """Heights other than 0, 64, 128, 224 and 256 are refused before any launch."""
     A = torch.zeros((256, 64), dtype=torch.bfloat16, device=DEV)
     B = torch.zeros((64, 256), dtype=torch.bfloat16, device=DEV)
     P = torch.zeros((1, 256, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(RuntimeError, match="invalid argument"):
-        gc.gemm_ar(A, B, P, R=2, rank=0, tile_rows=128)
+        gc.gemm_ar(A, B, P, R=2, rank=0, tile_rows=96)
