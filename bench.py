@@ -164,14 +164,28 @@ def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -
     bf16, then the reduction kernel gemm_coll_peer_sum over the rows this
     rank keeps (AR: all; RS and two-shot AR: its slice, the local product
     being the published partial; two-shot AR also copies the slice into the
-    R-1 peer outputs).  AG: one GEMM on the concatenated shards."""
+    R-1 peer outputs).  AG: the all-gather's data movement on one GPU -- a
+    copy of the R shards (the other ranks' from the receive buffer, this
+    rank's from A) into one [R*Ms, K] buffer -- then one GEMM on it."""
     import torch
     import tensor_bf16_gemm_amd as gc
     dev = x["B"].device
     B = x["B"]
     copies = None
+    pre = None
     if w.mode == "ag":
-        a_in = x["shards"].reshape(w.R * w.M, w.K)
+        gathered = torch.empty((w.R, w.M, w.K), dtype=torch.bfloat16, device=dev)
+        r = w.rank
+
+        def gather():
+            # contiguous slice copies (the other ranks' shards), then A
+            if r > 0:
+                gathered[:r].copy_(x["shards"][:r])
+            if r + 1 < w.R:
+                gathered[r + 1:].copy_(x["shards"][r + 1:])
+            gathered[r].copy_(x["A"])
+        pre = gather
+        a_in = gathered.view(w.R * w.M, w.K)
         local = torch.empty((w.R * w.M, w.N), dtype=torch.bfloat16, device=dev)
         reduce = None
     else:
@@ -191,6 +205,8 @@ def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -
     gemm = lambda: torch.matmul(a_in, B, out=local)
 
     def step():
+        if pre is not None:
+            pre()
         gemm()
         if reduce is not None:
             reduce()
@@ -213,10 +229,12 @@ def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -
     total = timed(step)
     res = {"us_per_step": total, "gemm_us": timed(gemm),
            "reduce_us": timed(reduce) if reduce is not None else 0.0,
+           "gather_us": timed(pre) if pre is not None else 0.0,
            "fused_speedup": total / fused_us,
            "what": "torch.matmul (hipBLASLt) to a bf16 local product, then gemm_coll_peer_sum"
                    + (" and the slice copies" if copies is not None else "")
-                   if w.mode != "ag" else "torch.matmul (hipBLASLt) on the concatenated shards",
+                   if w.mode != "ag" else "copy of the R shards into one buffer (the all-gather's "
+                   "data movement), then torch.matmul (hipBLASLt) on it",
            "steps": steps}
     return res
 
