@@ -200,6 +200,16 @@ def test_side_stream(orc):
                       "side stream AR")
 
 
+def test_default_stream_is_torch_current():
+    """stream=None launches on torch's current stream, also inside a
+    `with torch.cuda.stream(s)` block."""
+    assert gc._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert gc._stream(None) == s.cuda_stream
+    assert gc._stream(s) == s.cuda_stream
+
+
 # ---------------------------------------------------------------------------
 def test_invariants_between_modes():
     """RS rows == AR rows; AG == AR on the concatenated shards with zero
