@@ -386,7 +386,7 @@ def cpu_baseline(w, x, target_s: float):
         "cores": threads,
         "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of {total_rows} ({w.name}: all {w.N} columns, "
-                  f"K={w.K}{peers}); {dt:.1f} s; fp64 accumulation, plain loops",
+                  f"K={w.K}{peers}); {dt:.1f} s; {orc.acc} accumulation, plain loops",
         "seconds": dt,
         "rows": rows,
         "cpu": cpu_model(),

@@ -31,21 +31,30 @@
  *       AG-GEMM for Sequence Parallelism", Purpose).  The ring order in which
  *       a kernel consumes the shards does not change the result.
  *
- * Arithmetic: every bf16 input is decoded exactly to a double; products of
- * two bf16 values are exact in double; sums run in double in a fixed order
- * (k ascending, then peers ascending); the single rounding to bf16 is
- * round-to-nearest-even straight from the double (IEEE 754 roundTiesToEven
- * with an 8-bit significand and the binary32 exponent range).  The pages fix
- * bf16 operands and a bf16 result but not the accumulation precision of their
- * reference, so the oracle takes the nearly exact one.
+ * Arithmetic: every bf16 input is decoded exactly; the product of two bf16
+ * values (8 significant bits each) is exact in binary32 and in binary64; the
+ * sum runs in a fixed order (k ascending, then peers ascending) in one of two
+ * precisions, chosen per call by `acc`:
+ *   ORACLE_ACC_FP32  binary32 accumulator, each addition rounded to nearest
+ *                    even: the fp32 accumulation over bf16 inputs that the
+ *                    fused kernel's contract states (the default of the
+ *                    Python front end);
+ *   ORACLE_ACC_FP64  binary64 accumulator, nearly exact (for K and peer
+ *                    counts of these sizes the error is far below a bf16
+ *                    ulp), used to pin the fp32 one from outside.
+ * The single rounding to bf16 is round-to-nearest-even of the accumulator
+ * (IEEE 754 roundTiesToEven with an 8-bit significand and the binary32
+ * exponent range).  The pages fix bf16 operands and a bf16 result but print
+ * no accumulation precision for their reference.
  *
  * Rows are independent; OpenMP splits whole rows over threads, so the result
  * does not depend on the thread count.
  *
  * Planted-mistake builds (tests only): compiling with one of
  * -DORACLE_PLANT_{DROP_PEER,SKIP_LAST_K,SLICE_FLOOR,ROUND_TRUNC,AG_LOCAL_ONLY,
- * B_TRANSPOSED,WS_ALL_ROWS} introduces one plausible mistake, so that the
- * test suite can show that its pins catch it.  The default build has none.
+ * B_TRANSPOSED,WS_ALL_ROWS,ACC32_IN_DOUBLE,K_DESCENDING,PEERS_FIRST}
+ * introduces one plausible mistake, so that the test suite can show that its
+ * pins catch it.  The default build has none.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +64,10 @@
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-22)
 #define ORACLE_ENOMEM (-12)
+
+/* accumulation precision (argument `acc` of the entry points) */
+#define ORACLE_ACC_FP32 32
+#define ORACLE_ACC_FP64 64
 
 /* bf16 is the upper half of an IEEE binary32: decoding is a 16-bit shift. */
 static double bf16_to_double(uint16_t h)
@@ -66,6 +79,14 @@ static double bf16_to_double(uint16_t h)
 }
 
 double oracle_bf16_to_double(uint16_t h) { return bf16_to_double(h); }
+
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
 
 /*
  * Round a double to the nearest bf16, ties to even.
@@ -111,20 +132,27 @@ uint16_t oracle_round_bf16(double x)
  * a:      K bf16 values (one row of A)
  * B:      [K,N] row-major
  * peer_p: the row of peer p, at peer_rows + p*peer_stride
- * acc:    N doubles of scratch
+ * acc:    N accumulators of scratch (double or float, per `prec`)
+ * The terms are added one at a time in the order written: k = 0, 1, ...,
+ * K-1, then p = 0, 1, ..., npeers-1.  Each product a[k]*B[k,j] is exact in
+ * either precision, so the only roundings are those of the additions (and
+ * the final one to bf16).
  */
-static void oracle_row(const uint16_t *a, const uint16_t *B, const uint16_t *peer_rows,
-                       int64_t peer_stride, int npeers, int64_t N, int64_t K,
-                       double *acc, uint16_t *out)
+#ifdef ORACLE_PLANT_K_DESCENDING
+#define K_INDEX(t, kend) ((kend) - 1 - (t))
+#else
+#define K_INDEX(t, kend) (t)
+#endif
+
+static void gemm_terms_f64(const uint16_t *a, const uint16_t *B, int64_t N, int64_t K, double *acc)
 {
-    for (int64_t j = 0; j < N; ++j)
-        acc[j] = 0.0;
     int64_t kend = K;
 #ifdef ORACLE_PLANT_SKIP_LAST_K
     if (kend > 0)
         kend -= 1;
 #endif
-    for (int64_t k = 0; k < kend; ++k) {
+    for (int64_t t = 0; t < kend; ++t) {
+        int64_t k = K_INDEX(t, kend);
         double av = bf16_to_double(a[k]);
 #ifdef ORACLE_PLANT_B_TRANSPOSED
         /* reads B as if it were [N,K]: only meaningful when K == N */
@@ -136,18 +164,77 @@ static void oracle_row(const uint16_t *a, const uint16_t *B, const uint16_t *pee
             acc[j] += av * bf16_to_double(brow[j]);
 #endif
     }
+}
+
+static void gemm_terms_f32(const uint16_t *a, const uint16_t *B, int64_t N, int64_t K, float *acc)
+{
+    int64_t kend = K;
+#ifdef ORACLE_PLANT_SKIP_LAST_K
+    if (kend > 0)
+        kend -= 1;
+#endif
+    for (int64_t t = 0; t < kend; ++t) {
+        int64_t k = K_INDEX(t, kend);
+        float av = bf16_to_float(a[k]);
+#ifdef ORACLE_PLANT_B_TRANSPOSED
+        for (int64_t j = 0; j < N; ++j)
+            acc[j] += av * bf16_to_float(B[j * K + k]);
+#else
+        const uint16_t *brow = B + k * N;
+        for (int64_t j = 0; j < N; ++j)
+            acc[j] += av * bf16_to_float(brow[j]);
+#endif
+    }
+}
+
+static void oracle_row(const uint16_t *a, const uint16_t *B, const uint16_t *peer_rows,
+                       int64_t peer_stride, int npeers, int64_t N, int64_t K, int prec,
+                       void *scratch, uint16_t *out)
+{
     int np = npeers;
 #ifdef ORACLE_PLANT_DROP_PEER
     if (np > 0)
         np -= 1;
 #endif
-    for (int p = 0; p < np; ++p) {
-        const uint16_t *prow = peer_rows + (int64_t)p * peer_stride;
+#ifdef ORACLE_PLANT_ACC32_IN_DOUBLE
+    prec = ORACLE_ACC_FP64;
+#endif
+    if (prec == ORACLE_ACC_FP64) {
+        double *acc = (double *)scratch;
         for (int64_t j = 0; j < N; ++j)
-            acc[j] += bf16_to_double(prow[j]);
+            acc[j] = 0.0;
+#ifndef ORACLE_PLANT_PEERS_FIRST
+        gemm_terms_f64(a, B, N, K, acc);
+#endif
+        for (int p = 0; p < np; ++p) {
+            const uint16_t *prow = peer_rows + (int64_t)p * peer_stride;
+            for (int64_t j = 0; j < N; ++j)
+                acc[j] += bf16_to_double(prow[j]);
+        }
+#ifdef ORACLE_PLANT_PEERS_FIRST
+        gemm_terms_f64(a, B, N, K, acc);
+#endif
+        for (int64_t j = 0; j < N; ++j)
+            out[j] = oracle_round_bf16(acc[j]);
+    } else {
+        float *acc = (float *)scratch;
+        for (int64_t j = 0; j < N; ++j)
+            acc[j] = 0.0f;
+#ifndef ORACLE_PLANT_PEERS_FIRST
+        gemm_terms_f32(a, B, N, K, acc);
+#endif
+        for (int p = 0; p < np; ++p) {
+            const uint16_t *prow = peer_rows + (int64_t)p * peer_stride;
+            for (int64_t j = 0; j < N; ++j)
+                acc[j] += bf16_to_float(prow[j]);
+        }
+#ifdef ORACLE_PLANT_PEERS_FIRST
+        gemm_terms_f32(a, B, N, K, acc);
+#endif
+        /* a binary32 value is exactly a double: one rounding, to bf16 */
+        for (int64_t j = 0; j < N; ++j)
+            out[j] = oracle_round_bf16((double)acc[j]);
     }
-    for (int64_t j = 0; j < N; ++j)
-        out[j] = oracle_round_bf16(acc[j]);
 }
 
 /*
@@ -155,30 +242,33 @@ static void oracle_row(const uint16_t *a, const uint16_t *B, const uint16_t *pee
  *   A_rows    [nrows][K]          the sampled rows of A
  *   peer_rows [npeers][nrows][N]  the same rows of every peer partial
  *   out       [nrows][N]
+ *   acc       ORACLE_ACC_FP32 or ORACLE_ACC_FP64 (accumulation precision)
  * out[t,j] = bf16( sum_k A_rows[t,k]*B[k,j] + sum_p peer_rows[p,t,j] ).
  */
 int oracle_ar_rows(const uint16_t *A_rows, const uint16_t *B, const uint16_t *peer_rows,
-                   int64_t nrows, int64_t N, int64_t K, int npeers, uint16_t *out)
+                   int64_t nrows, int64_t N, int64_t K, int npeers, int acc, uint16_t *out)
 {
     if (nrows < 0 || N < 0 || K < 0 || npeers < 0)
+        return ORACLE_EINVAL;
+    if (acc != ORACLE_ACC_FP32 && acc != ORACLE_ACC_FP64)
         return ORACLE_EINVAL;
     if (npeers > 0 && !peer_rows)
         return ORACLE_EINVAL;
     int err = ORACLE_OK;
 #pragma omp parallel
     {
-        double *acc = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
-        if (!acc) {
+        void *scratch = malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!scratch) {
 #pragma omp atomic write
             err = ORACLE_ENOMEM;
         }
         /* every thread reaches the worksharing loop, with or without scratch */
 #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < nrows; ++t)
-            if (acc)
+            if (scratch)
                 oracle_row(A_rows + t * K, B, peer_rows ? peer_rows + t * N : NULL,
-                           nrows * N, npeers, N, K, acc, out + t * N);
-        free(acc);
+                           nrows * N, npeers, N, K, acc, scratch, out + t * N);
+        free(scratch);
     }
     return err;
 }
@@ -218,11 +308,11 @@ int oracle_rs_slice(int64_t M, int R, int r, int64_t *P, int64_t *lo, int64_t *h
  *   ascending rank order), out [M][N].
  */
 int oracle_gemm_ar(const uint16_t *A, const uint16_t *B, const uint16_t *peers,
-                   int64_t M, int64_t N, int64_t K, int R, uint16_t *out)
+                   int64_t M, int64_t N, int64_t K, int R, int acc, uint16_t *out)
 {
     if (R < 1 || M < 0)
         return ORACLE_EINVAL;
-    return oracle_ar_rows(A, B, peers, M, N, K, R - 1, out);
+    return oracle_ar_rows(A, B, peers, M, N, K, R - 1, acc, out);
 }
 
 /*
@@ -233,7 +323,7 @@ int oracle_gemm_ar(const uint16_t *A, const uint16_t *B, const uint16_t *peers,
  *               are left untouched.  ws may be NULL to skip the publish.
  */
 int oracle_gemm_rs(const uint16_t *A, const uint16_t *B, const uint16_t *peers,
-                   int64_t M, int64_t N, int64_t K, int R, int r,
+                   int64_t M, int64_t N, int64_t K, int R, int r, int acc,
                    uint16_t *out, uint16_t *ws)
 {
     int64_t P, lo, hi;
@@ -252,7 +342,7 @@ int oracle_gemm_rs(const uint16_t *A, const uint16_t *B, const uint16_t *peers,
                 memcpy(peer_rows + (int64_t)p * owned * N, peers + ((int64_t)p * M + lo) * N,
                        (size_t)owned * N * sizeof(uint16_t));
         }
-        err = oracle_ar_rows(A + lo * K, B, peer_rows, owned, N, K, R - 1, out);
+        err = oracle_ar_rows(A + lo * K, B, peer_rows, owned, N, K, R - 1, acc, out);
         free(peer_rows);
         if (err)
             return err;
@@ -263,17 +353,17 @@ int oracle_gemm_rs(const uint16_t *A, const uint16_t *B, const uint16_t *peers,
     /* publish the non-owned rows of this rank's partial */
     if (ws) {
 #ifdef ORACLE_PLANT_WS_ALL_ROWS
-        err = oracle_ar_rows(A, B, NULL, M, N, K, 0, ws);
+        err = oracle_ar_rows(A, B, NULL, M, N, K, 0, acc, ws);
         if (err)
             return err;
 #else
         if (lo > 0) {
-            err = oracle_ar_rows(A, B, NULL, lo, N, K, 0, ws);
+            err = oracle_ar_rows(A, B, NULL, lo, N, K, 0, acc, ws);
             if (err)
                 return err;
         }
         if (hi < M)
-            err = oracle_ar_rows(A + hi * K, B, NULL, M - hi, N, K, 0, ws + hi * N);
+            err = oracle_ar_rows(A + hi * K, B, NULL, M - hi, N, K, 0, acc, ws + hi * N);
 #endif
     }
     return err;
@@ -298,7 +388,7 @@ int oracle_ag_source(int64_t Ms, int R, int64_t g, int *q, int64_t *t)
  *   out     [R*Ms][N]  out[q*Ms + t] = bf16(S_q[t,:] . B)
  */
 int oracle_ag_gemm(const uint16_t *A_local, const uint16_t *B, const uint16_t *shards,
-                   int64_t Ms, int64_t N, int64_t K, int R, int r, uint16_t *out)
+                   int64_t Ms, int64_t N, int64_t K, int R, int r, int acc, uint16_t *out)
 {
     if (Ms < 0 || R < 1 || r < 0 || r >= R)
         return ORACLE_EINVAL;
@@ -307,7 +397,7 @@ int oracle_ag_gemm(const uint16_t *A_local, const uint16_t *B, const uint16_t *s
 #ifdef ORACLE_PLANT_AG_LOCAL_ONLY
         src = A_local;
 #endif
-        int err = oracle_ar_rows(src, B, NULL, Ms, N, K, 0, out + (int64_t)q * Ms * N);
+        int err = oracle_ar_rows(src, B, NULL, Ms, N, K, 0, acc, out + (int64_t)q * Ms * N);
         if (err)
             return err;
     }

@@ -10,7 +10,14 @@ What pins what:
   pin_rounding        IEEE round-to-nearest-even values worked out by hand,
                       and torch's float32 -> bf16 conversion (library routine)
   pin_brute_force     exact rational sums (fractions.Fraction) on tiny shapes:
-                      every oracle output is the nearest bf16, ties to even
+                      with the fp64 accumulator every output is the nearest
+                      bf16, ties to even; with the fp32 one it is the nearest
+                      bf16 of a value within the binary32 summation bound
+                      gamma_(n-1) * sum|terms| of the exact sum
+  pin_fp32_order      hand-worked binary32 sums where one rounding of the
+                      accumulator decides the bf16 result: the fp32 oracle
+                      must add k ascending, then the peers, in binary32 (and
+                      the fp64 one must give the exact answer)
   pin_integer_exact   small-integer inputs: the oracle equals exact integer
                       arithmetic (numpy int64 matmul) bit for bit
   pin_closed_forms    B = I gives A back; A = 0 gives the lone peer back;
@@ -108,26 +115,87 @@ def _nearest_check(exact: Fraction, h: int):
             assert (h & 1) == 0, f"tie at {float(exact)!r} not resolved to even"
 
 
+def _within_check(terms: list, h: int):
+    """h must be the nearest bf16 of some y with |y - S| <= gamma_(n-1) *
+    sum|terms|, S the exact sum of the n terms: the binary32 bound of a
+    recursive sum (each addition rounded to nearest, unit roundoff 2^-24),
+    whatever its order."""
+    exact = sum(terms, Fraction(0))
+    n = len(terms)
+    u = Fraction(1, 2 ** 24)
+    gamma = (n - 1) * u / (1 - (n - 1) * u) if n > 1 else Fraction(0)
+    err = gamma * sum(abs(t) for t in terms)
+    v = Fraction(decode(h))
+    # rounding interval of h: half-way to each finite neighbour
+    up = Fraction(decode((h + 1) & 0xFFFF)) if (h & 0x7FFF) < 0x7F7F else v
+    dn = Fraction(decode((h - 1) & 0xFFFF)) if (h & 0x7FFF) != 0 else -Fraction(decode(0x0001))
+    if h & 0x8000:
+        up, dn = dn, up
+    lo_r, hi_r = (v + min(up, dn)) / 2, (v + max(up, dn)) / 2
+    assert max(lo_r, exact - err) <= min(hi_r, exact + err), (
+        f"{h:#06x} is not the bf16 of any value within {float(err)!r} of {float(exact)!r}")
+
+
 def pin_brute_force(orc):
+    check = ((lambda terms, h: _nearest_check(sum(terms, Fraction(0)), h)) if orc.acc == "fp64"
+             else _within_check)
     rng = _rng(2)
-    for (M, N, K, R) in [(3, 5, 7, 2), (4, 6, 16, 4), (2, 3, 33, 3), (5, 4, 1, 2)]:
+    for (M, N, K, R) in [(3, 5, 7, 2), (4, 6, 16, 4), (2, 3, 33, 3), (5, 4, 1, 2), (2, 3, 200, 8)]:
         A = _rand_bf16(rng, (M, K), 1.0)
         B = _rand_bf16(rng, (K, N), 1.0 / np.sqrt(K))
         peers = _rand_bf16(rng, (R - 1, M, N), 1.0)
         out = orc.gemm_ar(A, B, peers, R)
         for i in range(M):
             for j in range(N):
-                s = sum(Fraction(decode(A[i, k])) * Fraction(decode(B[k, j])) for k in range(K))
-                s += sum(Fraction(decode(peers[p, i, j])) for p in range(R - 1))
-                _nearest_check(s, int(out[i, j]))
+                terms = [Fraction(decode(A[i, k])) * Fraction(decode(B[k, j])) for k in range(K)]
+                terms += [Fraction(decode(peers[p, i, j])) for p in range(R - 1)]
+                check(terms, int(out[i, j]))
     # K = N square case with structure that a transposed read would break
     A = _rand_bf16(rng, (3, 8), 1.0)
     B = _rand_bf16(rng, (8, 8), 1.0)
     out = orc.gemm_ar(A, B, np.zeros((1, 3, 8), np.uint16), 2)
     for i in range(3):
         for j in range(8):
-            s = sum(Fraction(decode(A[i, k])) * Fraction(decode(B[k, j])) for k in range(8))
-            _nearest_check(s, int(out[i, j]))
+            check([Fraction(decode(A[i, k])) * Fraction(decode(B[k, j])) for k in range(8)] +
+                  [Fraction(0)], int(out[i, j]))
+
+
+def pin_fp32_order(orc):
+    """Sums whose bf16 result depends on one binary32 rounding, worked out
+    by hand (IEEE 754 binary32: 24-bit significand, ties to even).
+
+    (a) 1.0625 * 1.0625 + 2^-15 * 2^-15 = (1 + 2^-3 + 2^-8) + 2^-30.  In
+        binary32 the second term is below half an ulp of the first (2^-24)
+        and is lost, leaving the exact bf16 tie 1.125 + 2^-8, which goes to
+        the even 1.125 (0x3F90).  The exact sum lies above the tie: 1.1328125
+        (0x3F91).
+    (b) k ascending over 2^12*2^12, 1*1, -2^12*2^12: 2^24 + 1 is a binary32
+        tie that goes to the even 2^24, then - 2^24 leaves 0 (0x0000).  The
+        exact sum, or k descending, gives 1 (0x3F80).
+    (c) the GEMM part 2^12*2^12 = 2^24, then peers 1 and -2^24: the same tie
+        leaves 0.  Peers first give -(2^24 - 1) + 2^24 = 1, the exact sum.
+    """
+    f32 = orc.acc == "fp32"
+    to = lambda xs: bits(torch.tensor(xs, dtype=torch.float64).to(torch.bfloat16))
+    A = to([[1.0625, 2.0 ** -15]])
+    B = to([[1.0625], [2.0 ** -15]])
+    got = int(orc.gemm_ar(A, B, np.zeros((1, 1, 1), np.uint16), 2)[0, 0])
+    want = 0x3F90 if f32 else 0x3F91
+    assert got == want, f"(a) lost low-order term: got {got:#06x}, want {want:#06x} ({orc.acc})"
+    A = to([[2.0 ** 12, 1.0, -2.0 ** 12]])
+    B = to([[2.0 ** 12], [1.0], [2.0 ** 12]])
+    got = int(orc.gemm_ar(A, B, np.zeros((1, 1, 1), np.uint16), 2)[0, 0])
+    want = 0x0000 if f32 else 0x3F80
+    assert got == want, f"(b) k order: got {got:#06x}, want {want:#06x} ({orc.acc})"
+    A = to([[2.0 ** 12]])
+    B = to([[2.0 ** 12]])
+    peers = to([[[1.0]], [[-2.0 ** 24]]])
+    got = int(orc.gemm_ar(A, B, peers, 3)[0, 0])
+    want = 0x0000 if f32 else 0x3F80
+    assert got == want, f"(c) peers after the GEMM part: got {got:#06x}, want {want:#06x} ({orc.acc})"
+    # the same through RS (rank 0 owns the single row) and AG (no peers: (a), (b))
+    o, _ = orc.gemm_rs(A, B, peers, 3, 0)
+    assert o.shape == (1, 1) and int(o[0, 0]) == want, f"(c) through RS ({orc.acc})"
 
 
 def pin_integer_exact(orc):
@@ -267,5 +335,5 @@ def pin_invariants(orc):
         assert q * Ms + t == g and 0 <= t < Ms
 
 
-ALL_PINS = [pin_rounding, pin_brute_force, pin_integer_exact, pin_closed_forms, pin_rs_golden,
-            pin_pages_reference, pin_invariants]
+ALL_PINS = [pin_rounding, pin_brute_force, pin_fp32_order, pin_integer_exact, pin_closed_forms,
+            pin_rs_golden, pin_pages_reference, pin_invariants]

@@ -3,8 +3,9 @@ oracle, and the whole unfused pipeline (library GEMM, then that kernel)
 against the fused entry point.
 
 The oracle has no separate peer-sum routine; ar_rows(I, L, peers) with the
-identity as A gives exactly bf16(L + sum of peers) in fp64, the definition
-the kernel follows (its fp32 sum is exact on integer inputs).  Cases: a
+identity as A gives bf16(L + sum of peers) with the sum taken in fp32 in the
+order local, peer 0, 1, ... (the identity adds only exact zeros), which is
+the definition the kernel follows.  Cases: a
 ragged element count (a tail of n % 8 elements), peer blocks farther apart
 than one block (a row slice of [R-1][M][N] partials), in place (out =
 local), no peers (a copy), and the largest peer count (15)."""
