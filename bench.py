@@ -158,15 +158,16 @@ def ingest_counters(name: str, fetch_dir: str, write_dir: str, cal_fetch_dir: st
     return entry
 
 
-def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -> dict:
-    """The unfused pipeline on the same inputs, timed like the fused kernel:
-    a library GEMM (torch.matmul, hipBLASLt) writing the local product in
-    bf16, then the reduction kernel gemm_coll_peer_sum over the rows this
-    rank keeps (AR: all; RS and two-shot AR: its slice, the local product
-    being the published partial; two-shot AR also copies the slice into the
-    R-1 peer outputs).  AG: the all-gather's data movement on one GPU -- a
-    copy of the R shards (the other ranks' from the receive buffer, this
-    rank's from A) into one [R*Ms, K] buffer -- then one GEMM on it."""
+def unfused_parts(w, x) -> dict:
+    """The unfused pipeline on the same inputs: a library GEMM (torch.matmul,
+    hipBLASLt) writing the local product in bf16, then the reduction kernel
+    gemm_coll_peer_sum over the rows this rank keeps (AR: all; RS and
+    two-shot AR: its slice, the local product being the published partial;
+    two-shot AR also copies the slice into the R-1 peer outputs).  AG: the
+    all-gather's data movement on one GPU -- a copy of the R shards (the
+    other ranks' from the receive buffer, this rank's from A) into one
+    [R*Ms, K] buffer -- then one GEMM on it.  Returns the whole step and its
+    parts as callables."""
     import torch
     import tensor_bf16_gemm_amd as gc
     dev = x["B"].device
@@ -213,30 +214,92 @@ def unfused_baseline(w, x, fused_us: float, steps: int = 30, warmup: int = 10) -
         if copies is not None:
             copies()
 
-    def timed(f):
-        for _ in range(warmup):
-            f()
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st = torch.cuda.current_stream()
-        s0.record(st)
-        for _ in range(steps):
-            f()
-        s1.record(st)
-        torch.cuda.synchronize()
-        return s0.elapsed_time(s1) / steps * 1e3
+    what = ("torch.matmul (hipBLASLt) to a bf16 local product, then gemm_coll_peer_sum"
+            + (" and the slice copies" if copies is not None else "")
+            if w.mode != "ag" else "copy of the R shards into one buffer (the all-gather's "
+            "data movement), then torch.matmul (hipBLASLt) on it")
+    return {"step": step, "gemm": gemm, "reduce": reduce, "gather": pre, "what": what}
 
-    total = timed(step)
-    res = {"us_per_step": total, "gemm_us": timed(gemm),
-           "reduce_us": timed(reduce) if reduce is not None else 0.0,
-           "gather_us": timed(pre) if pre is not None else 0.0,
-           "fused_speedup": total / fused_us,
-           "what": "torch.matmul (hipBLASLt) to a bf16 local product, then gemm_coll_peer_sum"
-                   + (" and the slice copies" if copies is not None else "")
-                   if w.mode != "ag" else "copy of the R shards into one buffer (the all-gather's "
-                   "data movement), then torch.matmul (hipBLASLt) on it",
-           "steps": steps}
-    return res
+
+def read_sclk() -> list:
+    """Active shader-clock levels (MHz) of the driver's sysfs tables
+    pp_dpm_sclk (the lines marked '*'); empty where they are not readable.
+    (A file read: no other program is started from this process.)"""
+    import glob
+    import re
+    out = []
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                for line in fh:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            out.append(int(m.group(1)))
+        except OSError:
+            pass
+    return out
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else None
+
+
+def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 10,
+                          warm: int = 60) -> dict:
+    """Fused against unfused in one window, so that both see the same clock:
+    `warm` launches of each (a fixed warm-up, past the power-limit transient
+    of about 60 launches), then `blocks` timed blocks of `per_block` launches
+    alternating in the order F U U F F U U F ... (each leg equally often
+    first).  Each block is timed with HIP events on the launch stream; the
+    shader clock is read from sysfs while each block runs.  Reports the
+    median block of each leg, then times the unfused parts alone."""
+    import torch
+    parts = unfused_parts(w, x)
+    legs = {"fused": fused_step, "unfused": parts["step"]}
+    st = torch.cuda.current_stream()
+    for _ in range(warm):
+        fused_step()
+    for _ in range(warm):
+        parts["step"]()
+    torch.cuda.synchronize()
+    times = {"fused": [], "unfused": []}
+    clocks = {"fused": [], "unfused": []}
+    for b in range(blocks):
+        name = ("fused", "unfused", "unfused", "fused")[b % 4]
+        f = legs[name]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(per_block):
+            f()
+        clocks[name] += read_sclk()          # the block is still running
+        e1.record(st)
+        torch.cuda.synchronize()
+        times[name].append(e0.elapsed_time(e1) / per_block * 1e3)
+
+    def alone(f, n=20):
+        if f is None:
+            return 0.0
+        for _ in range(5):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(n):
+            f()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    fu, uu = _median(times["fused"]), _median(times["unfused"])
+    return {"fused_us": fu, "us_per_step": uu, "fused_speedup": uu / fu,
+            "fused_blocks_us": times["fused"], "unfused_blocks_us": times["unfused"],
+            "sclk_mhz_fused": _median(clocks["fused"]), "sclk_mhz_unfused": _median(clocks["unfused"]),
+            "gemm_us": alone(parts["gemm"]), "reduce_us": alone(parts["reduce"]),
+            "gather_us": alone(parts["gather"]), "what": parts["what"],
+            "method": f"one window: {warm} warm-up launches of each leg, then {blocks} blocks of "
+                      f"{per_block} launches alternating F U U F ...; median block per leg; sclk "
+                      "read from sysfs during each block"}
 
 
 def ag_arrival(w, x, resident_us: float, iters: int = 10, warmup: int = 3) -> dict:
@@ -309,39 +372,20 @@ def ag_arrival(w, x, resident_us: float, iters: int = 10, warmup: int = 3) -> di
 
 def sample_sclk(step, seconds: float = 1.0) -> dict | None:
     """The shader clock while the step runs back to back: the active level of
-    the driver's sysfs table pp_dpm_sclk (the line marked '*'), read half-way
-    through about `seconds` of launches.  (A file read: no other program is
-    started from this process.)  The chip is power-limited, so the clock
-    under load is below the 2.4 GHz of the peak figures.  None where the
-    file is not readable."""
-    import glob
-    import re
+    the driver's sysfs table pp_dpm_sclk, read half-way through about
+    `seconds` of launches.  The chip is power-limited, so the clock under
+    load is below the 2.4 GHz of the peak figures.  None where the file is
+    not readable."""
     import torch
-    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-    if not files:
+    if not read_sclk():
         return None
-
-    def read():
-        out = []
-        for f in files:
-            try:
-                with open(f) as fh:
-                    for line in fh:
-                        if "*" in line:
-                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
-                            if m:
-                                out.append(int(m.group(1)))
-            except OSError:
-                pass
-        return out
-
     t0 = time.perf_counter()
     samples = []
     while time.perf_counter() - t0 < seconds:
         for _ in range(8):
             step()
         if time.perf_counter() - t0 > seconds / 2 and len(samples) < 8:
-            samples.append(read())      # launches queued ahead keep the GPU busy
+            samples.append(read_sclk())      # launches queued ahead keep the GPU busy
         torch.cuda.synchronize()
     vals = [v for s_ in samples for v in s_]
     if not vals:
@@ -422,6 +466,9 @@ def main(argv=None) -> int:
                     help="AG only: skip the run with shards arriving during the call")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the unfused baseline (library GEMM + peer-sum kernel)")
+    ap.add_argument("--profile", action="store_true",
+                    help="for profiler runs: only the W warm-up and K timed steps (no unfused "
+                         "comparison, cold launches, clock sampling, arrival or CPU baseline)")
     ap.add_argument("--cold-launches", type=int, default=30,
                     help="launches timed one by one after a 512 MiB write that evicts the L2 "
                          "and last-level caches (0 = skip)")
@@ -431,6 +478,12 @@ def main(argv=None) -> int:
                     help="rocprofv3 --pmc run directories (FETCH_SIZE and WRITE_SIZE of this "
                          "benchmark, then of --calibrate-copy): write profiles/traffic.json")
     args = ap.parse_args(argv)
+    if args.profile:
+        # A profiler serializes dispatches: the AG arrival leg (a kernel that
+        # polls flags raised by copies on another stream) would then wait out
+        # its time-outs, and the other legs only add kernels to the trace.
+        args.no_cpu_baseline = args.no_clock = args.no_arrival = args.no_unfused = True
+        args.cold_launches = 0
 
     if args.ingest_counters:
         import workloads as wl
@@ -468,6 +521,12 @@ def main(argv=None) -> int:
     w = wl.WORKLOADS[name]
     x = wl.make_inputs(w, device="cuda")
     step = make_step(w, x)
+    # The fused-versus-unfused comparison runs first, in a window of its own
+    # with a fixed warm-up (see compare_fused_unfused).  The W warm-up steps
+    # and the K timed steps follow it directly.
+    comparison = None
+    if not args.no_unfused:
+        comparison = compare_fused_unfused(w, x, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -544,13 +603,16 @@ def main(argv=None) -> int:
             "timing": "HIP events on the launch stream around the timed steps",
         },
         "cold": cold,
+        "preceded_by": None if comparison is None else
+        "the fused/unfused comparison in unfused_baseline (its own warm-up and blocks), then "
+        "the W warm-up steps",
         "wall_s": wall,
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_clock:
         line["sclk"] = sample_sclk(step)
-    if not args.no_unfused:
-        line["unfused_baseline"] = unfused_baseline(w, x, ms * 1e3)
+    if comparison is not None:
+        line["unfused_baseline"] = comparison
     if w.mode == "ag" and not args.no_arrival:
         line["arrival"] = ag_arrival(w, x, ms * 1e3)
     if not args.no_cpu_baseline:

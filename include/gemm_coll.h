@@ -44,10 +44,13 @@
  *   i.e. R in {2, 4, 8, 16} (the validation chain of maybe_init_gemm_rs_ar,
  *   "[Kimi-K3] Extend GEMM-RS to GEMM-AR", 关键源码片段); 0 <= rank < R.
  * - Ownership: the caller owns every buffer, including the optional
- *   workspace.  The library allocates no device memory, never synchronizes,
- *   and keeps no mutable state besides a per-device cache of device
- *   properties and a per-device launch counter; calls are thread-safe (but a
- *   workspace serves one call at a time).  Work is enqueued on
+ *   workspace.  The library allocates no device memory and never
+ *   synchronizes.  Its only mutable state is a per-device cache of the
+ *   compute-unit count and a per-device launch counter (an atomic that
+ *   stamps each split launch with a new epoch, so that the workspace's
+ *   counters, flags and claim words are never reset); calls are thread-safe,
+ *   but a workspace serves one call at a time: two calls in flight at once
+ *   (on different streams) need two workspaces.  Work is enqueued on
  *   `stream` (a hipStream_t; NULL = the null stream) and is complete only
  *   when that stream is.  Outputs must not alias any input.
  * - Errors: a negative return means nothing was launched.
@@ -63,9 +66,12 @@
  *   claim, so no call can deadlock whatever the order in which workgroups
  *   get a compute unit.  If that last workgroup's own (guard) wait gives up,
  *   the tile is left unwritten and, when peers->status is not NULL, *status
- *   is set to GC_TIMEOUT_BASE + 16.  (For tests, the environment variable
- *   GEMM_COLL_SPLIT_WAIT_SPINS, read at each call, overrides how long the
- *   other workgroups wait before leaving their share to the last one.)
+ *   is set to GC_TIMEOUT_BASE + 16.  (For tests, gc_peers.split_wait_spins
+ *   sets how long the other workgroups wait before leaving their share to
+ *   the last one.)  The split state lives in the workspace (one slot per
+ *   compute unit); a launch never indexes past it: the host plans at most
+ *   one split unit per slot, and the kernel checks this again and does no
+ *   work (status GC_TIMEOUT_BASE + 16) if it ever did not hold.
  *
  * gemm_coll_peer_sum is not a fused path: it is the reduction step of the
  * unfused baseline (a library GEMM, then this kernel) that the fused entry
@@ -133,6 +139,11 @@ typedef struct gc_peers {
        slot p for rank (p < rank ? p : p + 1); receives this rank's reduced
        slice rows (see gemm_ar_two_shot).  Ignored by the other calls. */
     gc_bf16 *peer_out;
+    /* For tests of the K-split hand-over, optional: 0 = the default; n > 0 =
+       the workgroups sharing a split tile wait only n polls for one another
+       before leaving their share to the last of them (see "K-split
+       hand-over" above).  Results do not change. */
+    uint32_t split_wait_spins;
 } gc_peers;
 
 /*
@@ -188,7 +199,11 @@ int gemm_ar_two_shot(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, i
  * polls flags[q] (system-scope acquire) until the shard is ready.  A shard
  * still not ready after max_spins polls is skipped: its output rows are left
  * unwritten and *status is set to GC_TIMEOUT_BASE + q (the first such shard
- * wins).  *status is otherwise never written: the caller clears it.
+ * wins).  Once *status is non-zero, a tile whose shard is not ready is
+ * skipped at its first poll, without waiting, so a launch whose producer has
+ * stalled ends after about one waiting period.  *status is otherwise never
+ * written: the caller clears it (a non-zero *status at the start of a call
+ * makes that call skip, rather than wait for, any shard not yet ready).
  * A [Ms][K], peers->shards [R][Ms][K], flags [R], status, out [R*Ms][N].
  */
 int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K, int R, int rank,

@@ -9,9 +9,10 @@ HIP kernels.  PyTorch supplies device memory and the stream.
     out = ag_gemm(A, B, shards, flags, status, R=8, rank=3, epoch=1)
 
 Tensors are bf16, contiguous, on the current CUDA (HIP) device.  By default
-each call uses a per-device workspace (allocated once) that lets the kernel
-split leftover tiles along K; pass workspace=False to compute every tile
-whole, or a zero-filled uint8 tensor of workspace_bytes() of your own.  A failed
+each call uses a workspace that lets the kernel split leftover tiles along
+K, allocated once per (device, stream) pair, so that calls in flight on
+different streams never share one; pass workspace=False to compute every
+tile whole, or a zero-filled uint8 tensor of workspace_bytes() of your own.  A failed
 call raises RuntimeError with the library's message.  If the library is not
 built, the first call raises: there is no fallback path.
 """
@@ -49,6 +50,7 @@ class GcPeers(ctypes.Structure):
         ("workspace_bytes", ctypes.c_uint64),
         ("tile_rows", ctypes.c_uint32),
         ("peer_out", ctypes.c_void_p),
+        ("split_wait_spins", ctypes.c_uint32),
     ]
 
 
@@ -136,27 +138,52 @@ def workspace_bytes() -> int:
     return n
 
 
-def default_workspace(device=None):
-    """A zero-filled workspace for `device`, allocated once and reused.  It
-    serves one call at a time: calls on concurrent streams need their own."""
+def _workspace_key(device, stream) -> tuple[int, int]:
+    """(device index, hipStream_t handle) that a default workspace serves."""
     import torch
-    dev = torch.device("cuda", torch.cuda.current_device() if device is None else
-                       torch.device(device).index)
-    ws = _workspaces.get(dev.index)
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    with torch.cuda.device(idx):
+        return idx, _stream(stream)
+
+
+def default_workspace(device=None, stream=None):
+    """The zero-filled workspace of (device, stream), allocated on first use
+    and reused by every later call on that stream.  Calls on one stream run
+    one after another, so they never use it at the same time; a call on
+    another stream gets a workspace of its own.  The zero fill is complete
+    before this returns (a device synchronization, once per workspace), so
+    the first call may be on any stream."""
+    import torch
+    key = _workspace_key(device, stream)
+
+    def make():
+        with torch.cuda.device(key[0]):
+            ws = torch.zeros(workspace_bytes(), dtype=torch.uint8, device=f"cuda:{key[0]}")
+            torch.cuda.synchronize(key[0])
+        return ws
+    return _cached_workspace(key, make)
+
+
+def _cached_workspace(key: tuple[int, int], make):
+    """The workspace cached under key = (device, stream), made by make() on
+    first use."""
+    ws = _workspaces.get(key)
     if ws is None:
-        with torch.cuda.device(dev):
-            ws = torch.zeros(workspace_bytes(), dtype=torch.uint8, device=dev)
-        _workspaces[dev.index] = ws
+        ws = make()
+        _workspaces[key] = ws
     return ws
 
 
-def _ws_fields(workspace, device):
-    """(pointer, bytes) for gc_peers: workspace=None -> the default one,
-    False -> none (every tile computed whole), else a uint8 device tensor."""
+def _ws_fields(workspace, device, stream):
+    """(pointer, bytes) for gc_peers: workspace=None -> the default one of
+    (device, stream), False -> none (every tile computed whole), else a uint8
+    device tensor."""
     if workspace is False:
         return None, 0
     if workspace is None:
-        workspace = default_workspace(device)
+        workspace = default_workspace(device, stream)
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -189,7 +216,7 @@ def _stream(stream) -> int:
 
 
 def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None, workspace=None,
-            status=None, tile_rows: int = 0):
+            status=None, tile_rows: int = 0, split_wait_spins: int = 0):
     """GEMM-AR: out [M,N] = bf16(A.B + sum of partials [R-1,M,N])."""
     import torch
     M, K = A.shape
@@ -200,16 +227,17 @@ def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None, workspa
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (M, N))
-    wp, wb = _ws_fields(workspace, A.device)
+    wp, wb = _ws_fields(workspace, A.device, stream)
     peers = GcPeers(partials=_ptr(partials), workspace=wp, workspace_bytes=wb,
-                    status=_ptr(status), tile_rows=int(tile_rows))
+                    status=_ptr(status), tile_rows=int(tile_rows),
+                    split_wait_spins=int(split_wait_spins))
     _check(lib().gemm_ar(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_ar")
     return out
 
 
 def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None, workspace=None,
-            status=None, tile_rows: int = 0):
+            status=None, tile_rows: int = 0, split_wait_spins: int = 0):
     """GEMM-RS: out [ceil(M/R), N] = this rank's rows of bf16(A.B + sum of partials);
     ws [M,N] receives bf16(A.B) on the rows this rank does not own."""
     import torch
@@ -223,16 +251,17 @@ def gemm_rs(A, B, partials, ws, out=None, *, R: int, rank: int, stream=None, wor
     if out is None:
         out = torch.empty((P, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (P, N))
-    wp, wb = _ws_fields(workspace, A.device)
+    wp, wb = _ws_fields(workspace, A.device, stream)
     peers = GcPeers(partials=_ptr(partials), ws=_ptr(ws), workspace=wp, workspace_bytes=wb,
-                    status=_ptr(status), tile_rows=int(tile_rows))
+                    status=_ptr(status), tile_rows=int(tile_rows),
+                    split_wait_spins=int(split_wait_spins))
     _check(lib().gemm_rs(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_rs")
     return out
 
 
 def gemm_ar_two_shot(A, B, partials, ws, peer_out, out=None, *, R: int, rank: int, stream=None,
-                     workspace=None, status=None, tile_rows: int = 0):
+                     workspace=None, status=None, tile_rows: int = 0, split_wait_spins: int = 0):
     """GEMM-AR, two-shot: this rank's rows [r*P, min((r+1)*P, M)) of
     bf16(A.B + sum of partials) go to out [M,N] and to every slot of
     peer_out [R-1,M,N]; ws [M,N] receives bf16(A.B) on the other rows.  Rows
@@ -248,16 +277,18 @@ def gemm_ar_two_shot(A, B, partials, ws, peer_out, out=None, *, R: int, rank: in
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (M, N))
-    wp, wb = _ws_fields(workspace, A.device)
+    wp, wb = _ws_fields(workspace, A.device, stream)
     peers = GcPeers(partials=_ptr(partials), ws=_ptr(ws), workspace=wp, workspace_bytes=wb,
-                    status=_ptr(status), tile_rows=int(tile_rows), peer_out=_ptr(peer_out))
+                    status=_ptr(status), tile_rows=int(tile_rows), peer_out=_ptr(peer_out),
+                    split_wait_spins=int(split_wait_spins))
     _check(lib().gemm_ar_two_shot(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers),
                                   _ptr(out), _stream(stream)), "gemm_ar_two_shot")
     return out
 
 
 def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: int,
-            max_spins: int = 0, stream=None, workspace=None, tile_rows: int = 0):
+            max_spins: int = 0, stream=None, workspace=None, tile_rows: int = 0,
+            split_wait_spins: int = 0):
     """AG-GEMM: out [R*Ms, N] = bf16(concat(shards).B), A = this rank's shard [Ms,K].
     flags: int32 tensor [R] in device memory or pinned host memory (the kernel
     polls it with system-scope loads); status: int32 device tensor [1]."""
@@ -275,10 +306,11 @@ def ag_gemm(A, B, shards, flags, status, out=None, *, R: int, rank: int, epoch: 
     if out is None:
         out = torch.empty((R * Ms, N), dtype=torch.bfloat16, device=A.device)
     _bf16("out", out, (R * Ms, N))
-    wp, wb = _ws_fields(workspace, A.device)
+    wp, wb = _ws_fields(workspace, A.device, stream)
     peers = GcPeers(shards=_ptr(shards), flags=_ptr(flags), epoch=int(epoch) & 0xFFFFFFFF,
                     status=_ptr(status), max_spins=int(max_spins), workspace=wp,
-                    workspace_bytes=wb, tile_rows=int(tile_rows))
+                    workspace_bytes=wb, tile_rows=int(tile_rows),
+                    split_wait_spins=int(split_wait_spins))
     _check(lib().ag_gemm(_ptr(A), _ptr(B), Ms, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "ag_gemm")
     return out

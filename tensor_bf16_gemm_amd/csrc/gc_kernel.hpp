@@ -110,10 +110,14 @@ struct Args {
     // claims hold the launch epoch, so none of them is ever reset.
     int dp_tiles;
     int sk_tiles, sk_q, sk_chunk, sk_units;
-    unsigned long long *sk_count;  // [sk_tiles]: (epoch << 32) | arrivals
-    uint32_t *sk_claim;        // [sk_tiles][16]: epoch of the launch that claimed the share
-    uint32_t *sk_flags;        // [2 * sk_units]: epoch, partial valid
-    float *sk_part;            // [sk_units][BM*BN]
+    // Slots of the workspace: sk_slots tile slots (counter, claims) and as
+    // many unit slots (flags, partial).  A split launch with more units or
+    // tiles than slots, or more than 16 chunks, does no work (see the kernel).
+    int sk_slots;
+    unsigned long long *sk_count;  // [sk_slots]: (epoch << 32) | arrivals
+    uint32_t *sk_claim;        // [sk_slots][16]: epoch of the launch that claimed the share
+    uint32_t *sk_flags;        // [2 * sk_slots]: epoch, partial valid
+    float *sk_part;            // [sk_slots][BM*BN]
     uint32_t sk_epoch;
     uint32_t sk_max_spins;     // guard on waits that always end
     uint32_t sk_wait_spins;    // how long a unit waits for its tile's other units
@@ -133,6 +137,7 @@ constexpr int PSLOT = 16 * WN * 2;         // one peer block of a wave: 2 KiB
 // Loads a wave issues per step: stage DMA (2 of A + 2 of B) and peer item (2).
 constexpr int DMA_PER_STEP = 4, PEER_PER_ITEM = 2;
 constexpr int PART_FLOATS = BM * BN;       // one fp32 partial tile
+constexpr uint32_t PART_BYTES = PART_FLOATS * 4u;
 
 // Out-of-range offset for buffer accesses: every buffer addressed here is
 // < 2 GiB, so this offset is past num_records; loads return 0, stores drop.
@@ -295,6 +300,19 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 {
     static_assert(FMT == 8 || FMT == 7 || FMT == 4 || FMT == 2, "row blocks per wave");
     static_assert(!SPLIT || FMT != 7, "224-row tiles are never split");
+    if constexpr (SPLIT) {
+        // Every workspace index below stays inside the sk_slots slots when
+        // sk_units and sk_tiles fit and a tile has at most 16 chunks (one
+        // claim word each).  The host plans no other launch; a launch that
+        // breaks this anyway leaves at once in every workgroup (a uniform
+        // test, before any wait), writes no output and reports a failed
+        // hand-over, instead of touching memory past the workspace.
+        if (p.sk_units > p.sk_slots || p.sk_tiles > p.sk_slots || p.sk_q > 16) {
+            if (threadIdx.x == 0 && blockIdx.x == 0 && p.status)
+                atomicCAS(p.status, 0, 1000 + 16);
+            return;
+        }
+    }
     constexpr int FMt = FMT, WMt = 16 * FMT, BMt = 2 * WMt;
     constexpr int NSEG = 2 * FMt;          // hand-over segments per wave
     // One array per operand and stage: distinct LDS objects carry distinct
@@ -450,7 +468,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                             ok = 1;
                             break;
                         }
-                        if (++spins >= p.max_spins)
+                        // Once a time-out is recorded (by any workgroup),
+                        // a shard that is not ready is skipped at once: a
+                        // launch whose producer has stalled then takes about
+                        // one waiting period, not one per tile or per shard.
+                        if (++spins >= p.max_spins ||
+                            __hip_atomic_load(p.status, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) != 0)
                             break;
                         __builtin_amdgcn_s_sleep(8);
                     }
@@ -732,15 +756,18 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             const int nq = p.sk_q;
             const uint32_t lane16 = (uint32_t)ln * 16u;
             const uint32_t wave_off = (uint32_t)(wave * FMt * FN * 1024);
+            // The partial slots, as one buffer over the whole region: an
+            // offset past the last slot stores nothing and loads zeros.
+            const uint32_t part_region = (uint32_t)p.sk_slots * PART_BYTES;
             if (!bad) {
-                const __amdgpu_buffer_rsrc_t rp =
-                    make_rsrc(p.sk_part + (size_t)u * PART_FLOATS, PART_FLOATS * 4u);
+                const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.sk_part, part_region);
+                const uint32_t vo = lane16 + (uint32_t)u * PART_BYTES;
 #pragma unroll
                 for (int i = 0; i < FMt; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)lane16,
+                            __builtin_bit_cast(u32x4_t, acc[i][j]), rp, (int)vo,
                             (int)(wave_off + (uint32_t)((i * FN + j) * 1024)), CPOL_SYS);
             }
             signal_partial(bad ? 0u : 1u);
@@ -842,7 +869,7 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             // (unit t / ns, t % ns-th segment of smask) of 2 KiB per wave,
             // through a ring of eight 2 KiB slots in the wave's 16 KiB of the
             // idle stages, DEPTH items in flight.  Items past the end are
-            // loads from an empty range (they fill their slot with zeros).
+            // loads out of range (they fill their slot with zeros).
             const int ns = __builtin_popcount(smask);
             const int T = (nq - 1) * ns;
             const uint8_t *wst = (wave >> 1) == 0 ? sS0 : (wave >> 1) == 1 ? sS1
@@ -855,16 +882,17 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 return __builtin_ctz(mm);
             };
             constexpr int DEPTH = 6;
+            const u32x4_t rpart = make_rsrc4(p.sk_part, part_region);
             auto issue = [&](int t) {
                 const int pc = t / ns;
                 const int cp = pc < sc ? pc : pc + 1;
                 const int sg = seg_of(t - pc * ns);
-                const u32x4_t r = make_rsrc4(p.sk_part + (size_t)(cp * p.sk_tiles + stt) * PART_FLOATS,
-                                             t < T ? PART_FLOATS * 4u : 0u);
+                const uint32_t vo =
+                    t < T ? lane16 + (uint32_t)(cp * p.sk_tiles + stt) * PART_BYTES : OOB;
                 const uint32_t slot = ring + (uint32_t)((t & 7) * 2048);
                 const uint32_t so = wave_off + (uint32_t)(sg * 2048);
-                dma16_sys(r, slot, lane16, so);
-                dma16_sys(r, slot + 1024u, lane16, so + 1024u);
+                dma16_sys(rpart, slot, vo, so);
+                dma16_sys(rpart, slot + 1024u, vo, so + 1024u);
             };
 #pragma unroll
             for (int t = 0; t < DEPTH; ++t)

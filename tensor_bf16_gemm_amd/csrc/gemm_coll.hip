@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
@@ -77,15 +76,16 @@ int check_common(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64
 // workgroup, and fewer than G split tiles): an 8-byte arrival counter and 16
 // claim words per tile, two flag words per unit, then one fp32 partial tile
 // per unit.  Each part starts on a 256-byte boundary.
-int64_t a256(int64_t x) { return (x + 255) / 256 * 256; }
-int64_t count_bytes(int groups) { return a256((int64_t)groups * 8); }
-int64_t claim_bytes(int groups) { return a256((int64_t)groups * 16 * 4); }
-int64_t flag_bytes(int groups) { return a256((int64_t)groups * 8); }
-int64_t workspace_bytes_for(int groups)
+constexpr int64_t a256(int64_t x) { return (x + 255) / 256 * 256; }
+constexpr int64_t count_bytes(int groups) { return a256((int64_t)groups * 8); }
+constexpr int64_t claim_bytes(int groups) { return a256((int64_t)groups * 16 * 4); }
+constexpr int64_t flag_bytes(int groups) { return a256((int64_t)groups * 8); }
+constexpr int64_t workspace_bytes_for(int groups)
 {
     return count_bytes(groups) + claim_bytes(groups) + flag_bytes(groups) +
            (int64_t)groups * gc::PART_FLOATS * 4;
 }
+
 
 // Chunk size (K-steps, a multiple of 8) for a problem of `tiles` < groups
 // tiles, cut into q <= min(16, groups / tiles) chunks so that every unit has
@@ -288,7 +288,9 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
     // One 512-thread workgroup per CU (the kernel holds up to 160 KiB of
     // LDS); a persistent workgroup walks its list of tiles and segments.
     const int cus = cu_count(dev);
-    const bool ws_ok = peers->workspace != nullptr &&
+    // (A workspace of `cus` slots is addressed with 32-bit offsets: at most
+    // 4096 slots of 256 KiB.)
+    const bool ws_ok = peers->workspace != nullptr && cus <= 4096 &&
                        peers->workspace_bytes >= (uint64_t)workspace_bytes_for(cus);
     // Peer items (AR, RS) take 8 * peers consecutive K-steps of a whole
     // tile, from its first step on (measured at M=4096: shifting them per
@@ -322,17 +324,18 @@ int dispatch(gc::Args &a, const gc_peers *peers, hipStream_t stream)
         a.sk_claim = (uint32_t *)(ws + count_bytes(cus));
         a.sk_flags = (uint32_t *)(ws + count_bytes(cus) + claim_bytes(cus));
         a.sk_part = (float *)(ws + count_bytes(cus) + claim_bytes(cus) + flag_bytes(cus));
+        a.sk_slots = cus;
         a.sk_epoch = g_epoch[dev < kMaxDevices ? dev : 0].fetch_add(1) + 1;
         a.sk_max_spins = 1u << 22;
         // About 0.3 ms of polling: far more than the spread of the units'
         // arrival times when they run at once (measured: up to 25 us), short
         // when they do not.
         a.sk_wait_spins = 256;
-        // Test hook: GEMM_COLL_SPLIT_WAIT_SPINS overrides that limit (a limit
-        // of 1 makes nearly every unit give up at once, so that the last unit
-        // to arrive finishes their shares).
-        if (const char *e = getenv("GEMM_COLL_SPLIT_WAIT_SPINS"))
-            a.sk_wait_spins = (uint32_t)std::max(1L, strtol(e, nullptr, 10));
+        // For tests: peers->split_wait_spins overrides that limit (a limit of
+        // 1 makes nearly every unit give up at once, so that the last unit to
+        // arrive finishes their shares).
+        if (peers->split_wait_spins != 0)
+            a.sk_wait_spins = peers->split_wait_spins;
         // The last unit to arrive leaves the others about 30 us to claim
         // their shares (they see its flag and claim within a few us) before
         // it claims what is left.

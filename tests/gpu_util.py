@@ -48,15 +48,3 @@ def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):
         i = tuple(bad[0])
         raise AssertionError(f"{what}: {len(bad)} of {got.size} differ; first {i}: "
                              f"gpu={got[i]:#06x} ref={ref[i]:#06x}")
-
-
-def sample_rows(M: int, tile: int = 256, extra: int = 8, seed: int = 0,
-                must: tuple[int, ...] = ()) -> list[int]:
-    """Rows at tile edges, the ends, `must`, and a few seeded random rows."""
-    rows = {0, 1, M - 1, M - 2}
-    for b in range(tile, M, tile * max(1, M // tile // 6)):
-        rows |= {b - 1, b, b + 15, b + 16}
-    rows |= set(must)
-    rng = np.random.default_rng(seed)
-    rows |= set(int(x) for x in rng.integers(0, M, extra))
-    return sorted(r for r in rows if 0 <= r < M)

@@ -33,7 +33,8 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "gemm_coll_should_run",
+    assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm",
+                          "gemm_coll_should_run",
                           "gemm_coll_strerror", "gemm_coll_workspace_bytes",
                           "gemm_coll_peer_sum", "ag_push_shards", "gemm_coll_plan"}, names
     out = subprocess.run(["nm", "-D", "--defined-only", gc.LIB_PATH], capture_output=True,
@@ -53,8 +54,8 @@ def test_peers_struct_layout(tmp_path):
         "offsetof(gc_peers,partials),offsetof(gc_peers,ws),offsetof(gc_peers,shards),"
         "offsetof(gc_peers,flags),offsetof(gc_peers,epoch),offsetof(gc_peers,status),"
         "offsetof(gc_peers,max_spins),sizeof(gc_peers));"
-        "printf(\"%zu %zu %zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes),"
-        "offsetof(gc_peers,tile_rows),offsetof(gc_peers,peer_out));"
+        "printf(\"%zu %zu %zu %zu %zu\\n\",offsetof(gc_peers,workspace),offsetof(gc_peers,workspace_bytes),"
+        "offsetof(gc_peers,tile_rows),offsetof(gc_peers,peer_out),offsetof(gc_peers,split_wait_spins));"
         "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe),
@@ -64,7 +65,8 @@ def test_peers_struct_layout(tmp_path):
     P = gc.GcPeers
     py_vals = [P.partials.offset, P.ws.offset, P.shards.offset, P.flags.offset, P.epoch.offset,
                P.status.offset, P.max_spins.offset, ctypes.sizeof(P), P.workspace.offset,
-               P.workspace_bytes.offset, P.tile_rows.offset, P.peer_out.offset]
+               P.workspace_bytes.offset, P.tile_rows.offset, P.peer_out.offset,
+               P.split_wait_spins.offset]
     assert c_vals == py_vals
 
 
@@ -192,3 +194,28 @@ def push(L, src=PA, dst=PA + 0x100000, Ms=64, K=256, R=8, rank=3, flags=PA + 0x2
 def test_ag_push_invalid_arguments(L, kw):
     assert push(L, **kw) == gc.GC_EINVAL
 
+
+
+def test_default_workspace_keyed_by_device_and_stream():
+    """The binding's default workspaces: one per (device, stream) pair, made
+    once and reused, so that calls on two streams never share one."""
+    made = []
+
+    def maker(tag):
+        def make():
+            made.append(tag)
+            return object()
+        return make
+    saved = dict(gc._workspaces)
+    try:
+        gc._workspaces.clear()
+        a = gc._cached_workspace((0, 0), maker("a"))
+        b = gc._cached_workspace((0, 0x1234), maker("b"))
+        c = gc._cached_workspace((1, 0), maker("c"))
+        assert len({id(a), id(b), id(c)}) == 3
+        assert gc._cached_workspace((0, 0), maker("again")) is a
+        assert gc._cached_workspace((0, 0x1234), maker("again")) is b
+        assert made == ["a", "b", "c"]
+    finally:
+        gc._workspaces.clear()
+        gc._workspaces.update(saved)

@@ -10,7 +10,7 @@ import torch
 
 import tensor_bf16_gemm_amd as gc
 import workloads as wl
-from gpu_util import assert_bits_equal, assert_close, host_bits, log, sample_rows
+from gpu_util import assert_bits_equal, assert_close, host_bits, log
 from oracle.oracle import load as load_oracle
 
 pytestmark = pytest.mark.gpu
@@ -107,7 +107,8 @@ def test_ragged_rs_all_ranks(orc, M, N, K, R):
         check_rs_full(orc, xc, out, ws, R, rank, M, N)
 
 
-@pytest.mark.parametrize("Ms,N,K,R", [(150, 520, 200, 4), (64, 264, 72, 8), (257, 40, 64, 2)])
+@pytest.mark.parametrize("Ms,N,K,R", [(150, 520, 200, 4), (64, 264, 72, 8), (257, 40, 64, 2),
+                                     (37, 264, 136, 16)])
 def test_ragged_ag_all_ranks(orc, Ms, N, K, R):
     log(f"ragged AG Ms={Ms} N={N} K={K} R={R}")
     w = wl.Workload("ragged", "ag", Ms, N, K, R, 0, 1.0, 1 / np.sqrt(K), seed=Ms + K)
@@ -236,7 +237,6 @@ def test_invariants_between_modes():
     # the peer count (AR's peer items must fit in the K loop), and a split
     # changes the fp32 summation order
     Ms = 111
-    shards = x["A"][: R * Ms].reshape(R, Ms, K).contiguous() if M >= R * Ms else None
     g = torch.Generator().manual_seed(9)
     shards = torch.randn(R, Ms, K, generator=g).to(torch.bfloat16).to(DEV)
     cat = shards.reshape(R * Ms, K)
@@ -324,3 +324,99 @@ def test_ag_flag_set_late_by_host(orc):
     sh = npb(xc["shards"])
     assert_bits_equal(npb(out), orc.ag_gemm(sh[rank].copy(), npb(xc["B"]), sh, R, rank),
                       "AG with a late flag")
+
+
+@pytest.mark.parametrize("Ms,N,K,R", [(40, 264, 128, 16), (300, 520, 512, 16)])
+def test_ag_sixteen_ranks_integer_all_ranks(orc, Ms, N, K, R):
+    """AG-GEMM with the largest rank count: every rank's ring order, integer
+    inputs, bit-exact against the oracle."""
+    log(f"AG R=16 Ms={Ms} N={N} K={K}")
+    xc = wl.integer_inputs("ag", Ms, N, K, R, rank=0, seed=Ms + K)
+    x = to_dev(xc)
+    sh = npb(xc["shards"])
+    ref = orc.ag_gemm(sh[0].copy(), npb(xc["B"]), sh, R, 0)
+    for rank in range(R):
+        xr = dict(x, A=x["shards"][rank].contiguous())
+        out, status = run_ag(xr, R, rank)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert_bits_equal(npb(out), ref, f"AG R=16 rank {rank}")
+
+
+def test_ag_two_shards_withheld():
+    """Two shards never become ready: the first in ring order is the one
+    status names, both are left unwritten, the rest is exact."""
+    Ms, N, K, R, rank = 64, 264, 128, 8, 3
+    xc = wl.integer_inputs("ag", Ms, N, K, R, rank=rank, seed=22)
+    x = to_dev(xc)
+    epoch = 9
+    flags = torch.full((R,), epoch, dtype=torch.int32, device=DEV)
+    flags[5] = epoch - 1           # ring order from rank 3: 3 2 1 0 7 6 5 4
+    flags[6] = epoch - 1
+    out = filled((R * Ms, N))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, out, R=R, rank=rank, epoch=epoch,
+               max_spins=2000)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gc.GC_TIMEOUT_BASE + 6
+    got = npb(out)
+    rows = np.arange(R * Ms) // Ms
+    missing = (rows == 5) | (rows == 6)
+    assert np.all(got[missing] == SENTINEL)
+    sh = npb(xc["shards"])
+    ref = load_oracle().ag_gemm(sh[rank].copy(), npb(xc["B"]), sh, R, rank)
+    assert_bits_equal(got[~missing], ref[~missing], "AG other shards")
+
+
+def test_ag_skips_without_waiting_once_timed_out():
+    """With a time-out already recorded in *status, a shard that is not
+    ready is skipped at its first poll: the launch ends in far less than the
+    one-second-plus that max_spins = 2^20 polls would take, and status keeps
+    its first value."""
+    import time
+    Ms, N, K, R, rank = 128, 520, 256, 8, 0
+    xc = wl.integer_inputs("ag", Ms, N, K, R, rank=rank, seed=23)
+    x = to_dev(xc)
+    flags = torch.ones(R, dtype=torch.int32, device=DEV)
+    flags[4] = 0
+    status = torch.full((1,), gc.GC_TIMEOUT_BASE + 2, dtype=torch.int32, device=DEV)
+    out = filled((R * Ms, N))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, out, R=R, rank=rank, epoch=1,
+               max_spins=1 << 20)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"  launch with a stalled shard after a recorded time-out: {dt * 1e3:.1f} ms")
+    assert int(status.item()) == gc.GC_TIMEOUT_BASE + 2
+    assert dt < 0.3, f"the launch waited {dt:.3f} s for a shard after a recorded time-out"
+    got = npb(out)
+    rows = np.arange(R * Ms) // Ms
+    assert np.all(got[rows == 4] == SENTINEL)
+    sh = npb(xc["shards"])
+    ref = load_oracle().ag_gemm(sh[rank].copy(), npb(xc["B"]), sh, R, rank)
+    assert_bits_equal(got[rows != 4], ref[rows != 4], "AG other shards")
+
+
+def test_default_workspace_per_stream():
+    """Calls on two streams get two default workspaces; calls on one stream
+    reuse one.  Split launches on both streams at once stay exact."""
+    M, N, K, R = 256, 1040, 2048, 4
+    xc = wl.integer_inputs("ar", M, N, K, R, seed=24)
+    x = to_dev(xc)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    w1 = gc.default_workspace(stream=s1)
+    w2 = gc.default_workspace(stream=s2)
+    assert w1.data_ptr() != w2.data_ptr()
+    assert gc.default_workspace(stream=s1).data_ptr() == w1.data_ptr()
+    assert gc.plan("ar", M, N, K, R, cus=torch.cuda.get_device_properties(0).multi_processor_count)["units"] > 0
+    ref = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=0, workspace=False)
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(4):
+        for s in (s1, s2):
+            with torch.cuda.stream(s):
+                outs.append(gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=0, stream=s))
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert_bits_equal(npb(o), npb(ref), f"split launch {i} on two streams")

@@ -223,7 +223,7 @@ def test_tail_round_split_equals_whole(orc, mode, M, N, K, R):
     ("rs", 300, 1040, 4096, 4),    # 10 tiles, 8 chunks each (64 rows: 25 tiles, 8 chunks)
     ("ag", 100, 520, 1024, 4),     # 12 tiles, 4 chunks each (64 rows: 24 tiles, 4 chunks)
 ])
-def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R, rows):
+def test_split_units_that_give_up(orc, mode, M, N, K, R, rows):
     """The split hand-over's fallback, forced from the host: with the units'
     wait limited to one poll, nearly every unit that is not the last to
     arrive leaves its share, and the last one finishes it.  The result must
@@ -233,19 +233,16 @@ def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R, rows):
     xc = wl.integer_inputs(mode, M, N, K, R, rank=rank, seed=M + 7 * K)
     x = to_dev(xc)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    monkeypatch.setenv("GEMM_COLL_SPLIT_WAIT_SPINS", "1")
     if mode == "ar":
         split = gc.gemm_ar(x["A"], x["B"], x["peers"], filled((M, N)), R=R, rank=rank, status=status,
-                           tile_rows=rows)
+                           tile_rows=rows, split_wait_spins=1)
         torch.cuda.synchronize()
-        monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
         whole = gc.gemm_ar(x["A"], x["B"], x["peers"], R=R, rank=rank, workspace=False)
     elif mode == "rs":
         ws_s = filled((M, N))
         split = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_s, R=R, rank=rank, status=status,
-                           tile_rows=rows)
+                           tile_rows=rows, split_wait_spins=1)
         torch.cuda.synchronize()
-        monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
         ws_w = filled((M, N))
         whole = gc.gemm_rs(x["A"], x["B"], x["peers"], ws_w, R=R, rank=rank, workspace=False)
         torch.cuda.synchronize()
@@ -253,9 +250,8 @@ def test_split_units_that_give_up(orc, monkeypatch, mode, M, N, K, R, rows):
     else:
         flags = torch.ones(R, dtype=torch.int32, device=DEV)
         split = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, filled((R * M, N)), R=R,
-                           rank=rank, epoch=1, tile_rows=rows)
+                           rank=rank, epoch=1, tile_rows=rows, split_wait_spins=1)
         torch.cuda.synchronize()
-        monkeypatch.delenv("GEMM_COLL_SPLIT_WAIT_SPINS")
         st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
         whole = gc.ag_gemm(x["A"], x["B"], x["shards"], flags, st2, R=R, rank=rank, epoch=1,
                            workspace=False)
