@@ -59,6 +59,8 @@
  *     GC_ENOTSUP  a shape this kernel set cannot address (a buffer of 2 GiB
  *                 or more, or a size above INT32_MAX)
  *     GC_EIO      the HIP launch failed
+ *     GC_ENOSPC   gemm_ar_noalloc only: its static scratch is too small for
+ *                 the device
  *   M == 0 (or N == 0) is valid and launches nothing.
  * - K-split hand-over: the workgroups sharing a split tile wait for one
  *   another only a bounded time, and the last of them to finish its part of
@@ -92,6 +94,7 @@ typedef uint16_t gc_bf16;
 #define GC_EINVAL (-22)
 #define GC_ENOTSUP (-95)
 #define GC_EIO (-5)
+#define GC_ENOSPC (-28)
 /* AG-GEMM reports a shard whose ready flag never came as *status = GC_TIMEOUT_BASE + q. */
 #define GC_TIMEOUT_BASE 1000
 
@@ -157,6 +160,28 @@ typedef struct gc_peers {
  */
 int gemm_ar(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R, int rank,
             const gc_peers *peers, gc_bf16 *out, void *stream);
+
+/*
+ * GEMM-AR that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, result and
+ * launches as gemm_ar; peers->workspace and peers->workspace_bytes are
+ * ignored.  In their place the K-split state (arrival counters, claim words,
+ * flags and fp32 partial tiles) lives in a static device array of the
+ * library, 64 MiB + 20 KiB: the workspace for up to 256 compute units, one
+ * copy per device, zero at load and held until the process ends.  No
+ * problem size needs more; on a device with more than 256 compute units the
+ * call returns GC_ENOSPC and launches nothing.  Nothing is cleared between
+ * calls: every launch stamps its counters, flags and claims with a new
+ * epoch, so the state a previous call left behind is never mistaken for
+ * this call's.  All calls on one device share its array: two such calls in
+ * flight at the same time (on different streams, or from different host
+ * threads) race on it and may return wrong results; serialize them.  The
+ * first call on a device looks up the array's device address (no
+ * allocation); later calls only launch kernels.
+ */
+int gemm_ar_noalloc(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R,
+                    int rank, const gc_peers *peers, gc_bf16 *out, void *stream);
 
 /*
  * GEMM-RS.  P = ceil(M/R); rank r owns global rows [r*P, (r+1)*P) (the pages'

@@ -21,11 +21,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "ag_push_shards", "peer_sum",
+__all__ = ["gemm_ar", "gemm_ar_noalloc", "gemm_rs", "gemm_ar_two_shot", "ag_gemm", "ag_push_shards", "peer_sum",
            "should_run", "strerror", "plan",
            "lib", "GcPeers", "GcPlan",
            "workspace_bytes", "default_workspace",
-           "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_TIMEOUT_BASE"]
+           "LIB_PATH", "GC_OK", "GC_EINVAL", "GC_ENOTSUP", "GC_EIO", "GC_ENOSPC",
+           "GC_TIMEOUT_BASE"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm_coll.so")
 
@@ -33,6 +34,7 @@ GC_OK = 0
 GC_EINVAL = -22
 GC_ENOTSUP = -95
 GC_EIO = -5
+GC_ENOSPC = -28
 GC_TIMEOUT_BASE = 1000
 
 
@@ -84,7 +86,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         sig = [vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(GcPeers), vp, vp]
-        for name in ("gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"):
+        for name in ("gemm_ar", "gemm_ar_noalloc", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"):
             f = getattr(L, name)
             f.argtypes = sig
             f.restype = ctypes.c_int
@@ -233,6 +235,25 @@ def gemm_ar(A, B, partials, out=None, *, R: int, rank: int, stream=None, workspa
                     split_wait_spins=int(split_wait_spins))
     _check(lib().gemm_ar(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers), _ptr(out),
                          _stream(stream)), "gemm_ar")
+    return out
+
+
+def gemm_ar_noalloc(A, B, partials, out, *, R: int, rank: int, stream=None, status=None,
+                    tile_rows: int = 0):
+    """GEMM-AR that allocates nothing (gemm_ar_noalloc in the C ABI): as
+    gemm_ar, with the K-split state in the library's static per-device
+    scratch instead of a workspace.  `out` [M,N] is required (this wrapper
+    allocates nothing either).  Calls on one device share that scratch: do
+    not run two at the same time."""
+    M, K = A.shape
+    N = B.shape[1]
+    _bf16("A", A)
+    _bf16("B", B, (K, N))
+    _bf16("partials", partials, (R - 1, M, N))
+    _bf16("out", out, (M, N))
+    peers = GcPeers(partials=_ptr(partials), status=_ptr(status), tile_rows=int(tile_rows))
+    _check(lib().gemm_ar_noalloc(_ptr(A), _ptr(B), M, N, K, R, rank, ctypes.byref(peers),
+                                 _ptr(out), _stream(stream)), "gemm_ar_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "gc_kernel.hpp"
 #include "gemm_coll.h"
@@ -86,6 +87,37 @@ constexpr int64_t workspace_bytes_for(int groups)
            (int64_t)groups * gc::PART_FLOATS * 4;
 }
 
+// The split state of gemm_ar_noalloc: the workspace layout above for up to
+// kScratchSlots compute units (256, MI355X's count: 64 MiB + 20 KiB), in
+// device memory of the code object itself, one copy per device, zero at
+// load and held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (in host code the name stands for a host-side shadow,
+// not a device address): scratch_address() looks up each device's copy
+// once, with that device current, and calls use that address.
+constexpr int kScratchSlots = 256;
+constexpr int64_t kScratchBytes = workspace_bytes_for(kScratchSlots);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];   // device address, per device
+
+int scratch_address(int dev, void **out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return GC_ENOTSUP;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return GC_EIO;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return GC_OK;
+}
 
 // Chunk size (K-steps, a multiple of 8) for a problem of `tiles` < groups
 // tiles, cut into q <= min(16, groups / tiles) chunks so that every unit has
@@ -471,6 +503,9 @@ const char *gemm_coll_strerror(int code)
         return "shape not supported by this kernel set (a buffer of 2 GiB or more)";
     case GC_EIO:
         return "HIP kernel launch failed";
+    case GC_ENOSPC:
+        return "gemm_ar_noalloc: the library's static scratch (split state for up to 256 "
+               "compute units) is smaller than this device needs";
     default:
         if (code >= GC_TIMEOUT_BASE && code < GC_TIMEOUT_BASE + 16)
             return "AG-GEMM: a shard's ready flag did not arrive in time";
@@ -502,6 +537,36 @@ int gemm_ar(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K,
     a.m_rows = (int)M;
     a.status = peers->status;
     return dispatch<gc::MODE_AR>(a, peers, (hipStream_t)stream);
+}
+
+int gemm_ar_noalloc(const gc_bf16 *A, const gc_bf16 *B, int64_t M, int64_t N, int64_t K, int R,
+                    int rank, const gc_peers *peers, gc_bf16 *out, void *stream)
+{
+    // The checks of gemm_ar first, so that invalid calls fail before any
+    // device call.
+    int err = check_common(A, B, M, N, K, R, rank, peers, out);
+    if (err || M == 0 || N == 0)
+        return err;
+    if (!peers->partials || !aligned16(peers->partials))
+        return GC_EINVAL;
+    if (!fits(M, K) || !fits(K, N) || !fits(M, N))
+        return GC_ENOTSUP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GC_EIO;
+    // The split state of a call needs workspace_bytes_for(compute units):
+    // no problem size needs more, and the scratch holds it for up to
+    // kScratchSlots units.
+    if (workspace_bytes_for(cu_count(dev)) > kScratchBytes)
+        return GC_ENOSPC;
+    void *ws = nullptr;
+    err = scratch_address(dev, &ws);
+    if (err)
+        return err;
+    gc_peers p = *peers;
+    p.workspace = ws;
+    p.workspace_bytes = (uint64_t)kScratchBytes;
+    return gemm_ar(A, B, M, N, K, R, rank, &p, out, stream);
 }
 
 // GEMM-RS, or (two_shot) the two-shot GEMM-AR that extends it.

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert set(names) == {"gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm",
+    assert set(names) == {"gemm_ar", "gemm_ar_noalloc", "gemm_rs", "gemm_ar_two_shot", "ag_gemm",
                           "gemm_coll_should_run",
                           "gemm_coll_strerror", "gemm_coll_workspace_bytes",
                           "gemm_coll_peer_sum", "ag_push_shards", "gemm_coll_plan"}, names
@@ -93,7 +93,8 @@ def test_should_run_gate(L):
 
 
 def test_strerror(L):
-    for code in (gc.GC_OK, gc.GC_EINVAL, gc.GC_ENOTSUP, gc.GC_EIO, gc.GC_TIMEOUT_BASE + 3, 12345):
+    for code in (gc.GC_OK, gc.GC_EINVAL, gc.GC_ENOTSUP, gc.GC_EIO, gc.GC_ENOSPC,
+                 gc.GC_TIMEOUT_BASE + 3, 12345):
         s = gc.strerror(code)
         assert isinstance(s, str) and s
     assert "flag" in gc.strerror(gc.GC_TIMEOUT_BASE + 3)
@@ -112,7 +113,7 @@ def call(L, name, A=PA, B=PA + 0x100000, M=256, N=256, K=256, R=8, rank=0, out=P
     return getattr(L, name)(A, B, M, N, K, R, rank, ctypes.byref(p) if peers else None, out, None)
 
 
-ALL = ["gemm_ar", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"]
+ALL = ["gemm_ar", "gemm_ar_noalloc", "gemm_rs", "gemm_ar_two_shot", "ag_gemm"]
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -129,6 +130,7 @@ def test_invalid_arguments(L, name, kw):
 
 @pytest.mark.parametrize("name,kw", [
     ("gemm_ar", dict(partials=None)), ("gemm_ar", dict(partials=PA + 0x300008)),
+    ("gemm_ar_noalloc", dict(partials=None)), ("gemm_ar_noalloc", dict(partials=PA + 0x300008)),
     ("gemm_rs", dict(partials=None)), ("gemm_rs", dict(ws=None)), ("gemm_rs", dict(ws=PA + 2)),
     ("ag_gemm", dict(shards=None)), ("ag_gemm", dict(flags=None)), ("ag_gemm", dict(flags=PA + 2)),
     ("ag_gemm", dict(status=None)), ("ag_gemm", dict(shards=PA + 0x500004)),
