@@ -246,7 +246,7 @@ def _median(v):
     return v[len(v) // 2] if v else None
 
 
-def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 10,
+def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 20,
                           warm: int = 60) -> dict:
     """Fused against unfused in one window, so that both see the same clock:
     `warm` launches of each (a fixed warm-up, past the power-limit transient
@@ -254,16 +254,22 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 1
     alternating in the order F U U F F U U F ... (each leg equally often
     first).  Each block is timed with HIP events on the launch stream; the
     shader clock is read from sysfs while each block runs.  Reports the
-    median block of each leg, then times the unfused parts alone."""
+    median block of each leg, then times the unfused parts alone.  (The
+    clock is read half-way through each block, by the warm-up's time per
+    launch.)"""
     import torch
     parts = unfused_parts(w, x)
     legs = {"fused": fused_step, "unfused": parts["step"]}
     st = torch.cuda.current_stream()
-    for _ in range(warm):
-        fused_step()
-    for _ in range(warm):
-        parts["step"]()
-    torch.cuda.synchronize()
+    est = {}
+    for name, f in legs.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(warm):
+            f()
+        e1.record(st)
+        torch.cuda.synchronize()
+        est[name] = e0.elapsed_time(e1) / warm * 1e-3      # seconds per launch
     times = {"fused": [], "unfused": []}
     clocks = {"fused": [], "unfused": []}
     for b in range(blocks):
@@ -273,8 +279,11 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 1
         e0.record(st)
         for _ in range(per_block):
             f()
-        clocks[name] += read_sclk()          # the block is still running
         e1.record(st)
+        # Read the clock while the block runs, half-way through (the read
+        # itself takes milliseconds; the events are already enqueued).
+        time.sleep(0.5 * per_block * est[name])
+        clocks[name] += read_sclk()
         torch.cuda.synchronize()
         times[name].append(e0.elapsed_time(e1) / per_block * 1e3)
 

@@ -344,8 +344,10 @@ def test_ag_sixteen_ranks_integer_all_ranks(orc, Ms, N, K, R):
 
 
 def test_ag_two_shards_withheld():
-    """Two shards never become ready: the first in ring order is the one
-    status names, both are left unwritten, the rest is exact."""
+    """Two shards never become ready: status names one of them (their tiles
+    are polled by different workgroups at the same time, and the first to
+    time out records its shard), both are left unwritten, the rest is
+    exact."""
     Ms, N, K, R, rank = 64, 264, 128, 8, 3
     xc = wl.integer_inputs("ag", Ms, N, K, R, rank=rank, seed=22)
     x = to_dev(xc)
@@ -358,7 +360,7 @@ def test_ag_two_shards_withheld():
     gc.ag_gemm(x["A"], x["B"], x["shards"], flags, status, out, R=R, rank=rank, epoch=epoch,
                max_spins=2000)
     torch.cuda.synchronize()
-    assert int(status.item()) == gc.GC_TIMEOUT_BASE + 6
+    assert int(status.item()) in (gc.GC_TIMEOUT_BASE + 5, gc.GC_TIMEOUT_BASE + 6)
     got = npb(out)
     rows = np.arange(R * Ms) // Ms
     missing = (rows == 5) | (rows == 6)
