@@ -105,33 +105,43 @@ def read_traffic(w, kernel_us: float):
 
 def _counter_means(run_dir: str, counter: str) -> dict:
     """Mean value of `counter` per kernel name over the dispatches recorded in
-    a rocprofv3 --pmc run directory (its *counter_collection.csv files)."""
+    a rocprofv3 --pmc run directory (its *counter_collection.csv files); rows
+    of one dispatch (one per counter instance, where the tool splits them)
+    are summed first."""
     import csv
     import glob
-    vals: dict = {}
+    per: dict = {}
     for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] == counter:
-                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                    key = (f, r["Dispatch_Id"])
+                    name, v = per.get(key, (r["Kernel_Name"], 0.0))
+                    per[key] = (name, v + float(r["Counter_Value"]))
+    vals: dict = {}
+    for name, v in per.values():
+        vals.setdefault(name, []).append(v)
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
 def ingest_counters(name: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str,
                     cal_write_dir: str) -> dict:
-    """HBM bytes per launch of the fused kernel from four rocprofv3 --pmc runs:
+    """HBM bytes per step of the fused path from four rocprofv3 --pmc runs:
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of this benchmark, and the
     same two counters for `--calibrate-copy` (a 1 GiB device copy, so 1 GiB
     read and 1 GiB written).  Each counter is divided by what it reads for the
-    copy per byte moved.  Writes the entry into profiles/traffic.json."""
+    copy per byte moved.  A step is one launch of each gc_kernel instance the
+    call makes (two where full rounds of whole tiles precede a split tail),
+    so the per-instance means are summed.  Writes the entry into
+    profiles/traffic.json."""
     n = 1 << 30
 
     def kernel_kib(d, counter):
         m = _counter_means(d, counter)
         ks = [k for k in m if "gc_kernel" in k]
-        if len(ks) != 1:
-            raise SystemExit(f"{d}: expected one gc_kernel entry for {counter}, found {ks}")
-        return m[ks[0]]
+        if not ks:
+            raise SystemExit(f"{d}: no gc_kernel entry for {counter}")
+        return sum(m[k] for k in ks), {k: m[k] for k in ks}
 
     def copy_kib(d, counter):
         m = _counter_means(d, counter)
@@ -141,11 +151,16 @@ def ingest_counters(name: str, fetch_dir: str, write_dir: str, cal_fetch_dir: st
 
     f_fetch = copy_kib(cal_fetch_dir, "FETCH_SIZE") * 1024 / n
     f_write = copy_kib(cal_write_dir, "WRITE_SIZE") * 1024 / n
-    fetch = kernel_kib(fetch_dir, "FETCH_SIZE") * 1024 / f_fetch
-    write = kernel_kib(write_dir, "WRITE_SIZE") * 1024 / f_write
+    fk, fparts = kernel_kib(fetch_dir, "FETCH_SIZE")
+    wk, wparts = kernel_kib(write_dir, "WRITE_SIZE")
+    fetch = fk * 1024 / f_fetch
+    write = wk * 1024 / f_write
     entry = {"source_digest": source_digest(), "bytes_per_launch": fetch + write,
              "fetch_bytes": fetch, "write_bytes": write,
-             "copy_factor_fetch": f_fetch, "copy_factor_write": f_write}
+             "copy_factor_fetch": f_fetch, "copy_factor_write": f_write,
+             "instances": {k: {"fetch_bytes": fparts[k] * 1024 / f_fetch,
+                               "write_bytes": wparts.get(k, 0.0) * 1024 / f_write}
+                           for k in fparts}}
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
