@@ -60,6 +60,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -275,6 +277,20 @@ __device__ __forceinline__ void barrier_only()
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// f(0), f(1), ..., f(7), each index a compile-time constant.
+template <class F>
+__device__ __forceinline__ void unroll8(F &&f)
+{
+    f(std::integral_constant<int, 0>{});
+    f(std::integral_constant<int, 1>{});
+    f(std::integral_constant<int, 2>{});
+    f(std::integral_constant<int, 3>{});
+    f(std::integral_constant<int, 4>{});
+    f(std::integral_constant<int, 5>{});
+    f(std::integral_constant<int, 6>{});
+    f(std::integral_constant<int, 7>{});
 }
 
 // Logical tile of workgroup `b` in one round of `G` workgroups.  Workgroups
@@ -674,49 +690,80 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // complete and every stage about to be read has landed.
         // The loop is unrolled by 8 so that the stage, the peer slot and the
         // peer row block are compile-time constants.
+        //
+        // The peer items of a segment take its first steps: the window
+        // [wlo, whi) starts at g0.  Steps [g0, E), E the end of the window
+        // rounded up to whole groups of 8, run as above; the steps after E
+        // issue no peer loads at all (no empty ones either).  Their waits
+        // for stage kt+1 then count only the stage loads after it, except in
+        // steps E and E+1, when the empty loads of items E and E+1 (issued
+        // in steps E-2 and E-1) are still younger than it.
         constexpr int AFTER = 2 * DMA_PER_STEP + (PEERS ? 3 * PEER_PER_ITEM : 0);
         const bool lag = wave >= 4;
         wait_vmcnt<AFTER>();          // own loads of stage 0 done
         if (lag)
             barrier_only();
-        for (int kt0 = g0; kt0 < g1; kt0 += 8) {
+        // ITEMS: the step adds item kt and loads item kt+2; otherwise tr is
+        // the step's distance from E (0, 1, or 2 for any later step).
+        auto step = [&](auto uc, auto items_c, int kt, int tr) {
+            constexpr int u = decltype(uc)::value;
+            constexpr bool ITEMS = PEERS && decltype(items_c)::value;
+            uint8_t *cS = (u & 3) == 0 ? sS0 : (u & 3) == 1 ? sS1 : (u & 3) == 2 ? sS2 : sS3;
+            uint8_t *nS = (u & 3) == 0 ? sS3 : (u & 3) == 1 ? sS0 : (u & 3) == 2 ? sS1 : sS2;
+            uint8_t *cA = cS, *nA = nS, *nB = nS + A_BYTES;
+            uint8_t *sl = (u & 1) ? sP1 : sP0;
+            // ---- M(kt) ----
+            barrier_only();
+            bf16x8_t fa[FN], fb[FMt];
+            read_frags(cA, fa, fb);
+            dma_stage(kt + 3, nA, nB);
+            if constexpr (ITEMS) {
+                // Item kt was issued in M(kt-2); after it came stage
+                // kt+2, item kt+1 and stage kt+3.
+                wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
+                if (u < FMt && kt >= wlo && kt < whi) {
+                    u32x2_t pv[FN];
+                    const uint32_t pb = opaque(lds_addr(sl)) + wave * PSLOT;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int kt = kt0 + u;
-                if (kt < g1) {
-                    uint8_t *cS = (u & 3) == 0 ? sS0 : (u & 3) == 1 ? sS1 : (u & 3) == 2 ? sS2 : sS3;
-                    uint8_t *nS = (u & 3) == 0 ? sS3 : (u & 3) == 1 ? sS0 : (u & 3) == 2 ? sS1 : sS2;
-                    uint8_t *cA = cS, *cB = cS + A_BYTES, *nA = nS, *nB = nS + A_BYTES;
-                    uint8_t *sl = (u & 1) ? sP1 : sP0;
-                    // ---- M(kt) ----
-                    barrier_only();
-                    bf16x8_t fa[FN], fb[FMt];
-                    read_frags(cA, fa, fb);
-                    dma_stage(kt + 3, nA, nB);
-                    if (PEERS) {
-                        // Item kt was issued in M(kt-2); after it came stage
-                        // kt+2, item kt+1 and stage kt+3.
-                        wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
-                        if (u < FMt && kt >= wlo && kt < whi) {
-                            u32x2_t pv[FN];
-                            const uint32_t pb = opaque(lds_addr(sl)) + wave * PSLOT;
+                    for (int j = 0; j < FN; ++j)
+                        pv[j] = *lds_ptr<u32x2_t>(pb + (pc_off ^ (uint32_t)(32 * j)));
 #pragma unroll
-                            for (int j = 0; j < FN; ++j)
-                                pv[j] = *lds_ptr<u32x2_t>(pb + (pc_off ^ (uint32_t)(32 * j)));
-#pragma unroll
-                            for (int j = 0; j < FN; ++j)
-                                acc[u % FMt][j] += unpack_bf16x4(pv[j]);
-                        }
-                        wait_lgkmcnt0();  // slot read back before it is refilled
-                        peer_dma(sl, kt + 2, (u + 2) & 7, pd_off, pd_n);
-                    }
-                    wait_vmcnt<AFTER>();  // own loads of stage kt+1 done
-                    wait_lgkmcnt0();      // stage kt fully read into registers
-                    // ---- C(kt) ----
-                    barrier_only();
-                    mfmas(fa, fb);
+                    for (int j = 0; j < FN; ++j)
+                        acc[u % FMt][j] += unpack_bf16x4(pv[j]);
                 }
+                wait_lgkmcnt0();  // slot read back before it is refilled
+                peer_dma(sl, kt + 2, (u + 2) & 7, pd_off, pd_n);
+                wait_vmcnt<AFTER>();  // own loads of stage kt+1 done
+            } else if constexpr (PEERS) {
+                if (tr == 0)
+                    wait_vmcnt<2 * DMA_PER_STEP + 2 * PEER_PER_ITEM>();
+                else if (tr == 1)
+                    wait_vmcnt<2 * DMA_PER_STEP + PEER_PER_ITEM>();
+                else
+                    wait_vmcnt<2 * DMA_PER_STEP>();
+            } else {
+                wait_vmcnt<AFTER>();
             }
+            wait_lgkmcnt0();      // stage kt fully read into registers
+            // ---- C(kt) ----
+            barrier_only();
+            mfmas(fa, fb);
+        };
+        const int E = PEERS ? min(g1, g0 + ((max(whi - g0, 0) + 7) & ~7)) : g0;
+        for (int kt0 = g0; kt0 < E; kt0 += 8)
+            unroll8([&](auto uc) {
+                const int kt = kt0 + decltype(uc)::value;
+                if (kt < E)
+                    step(uc, std::true_type{}, kt, 0);
+            });
+        for (int kt0 = E; kt0 < g1; kt0 += 8) {
+            const bool first = kt0 == E;
+            unroll8([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                const int kt = kt0 + u;
+                if (kt < g1)
+                    step(uc, std::false_type{}, kt, first ? (u < 2 ? u : 2) : 2);
+            });
         }
         if (!lag)
             barrier_only();           // same barrier count in both groups
