@@ -277,7 +277,9 @@ def test_ag_flags_withheld_times_out(orc):
 
 def test_ag_epochs_and_fresh_data(orc):
     """Flags are never reset: a later call with epoch+1 and new shard
-    content must see the new content."""
+    content must see the new content.  The new shards and the raised flags
+    arrive through the DMA engines (ag_push_shards), not through kernels,
+    so a cached copy of the first call's shards would show."""
     Ms, N, K, R, rank = 64, 136, 64, 4, 1
     xc = wl.integer_inputs("ag", Ms, N, K, R, rank=rank, seed=31)
     x = to_dev(xc)
@@ -286,9 +288,10 @@ def test_ag_epochs_and_fresh_data(orc):
     torch.cuda.synchronize()
     assert int(st1.item()) == 0
     new_shards = (-xc["shards"]).contiguous()
-    x["shards"].copy_(new_shards.to(DEV))
+    src = new_shards.to(DEV)
+    ew = torch.full((1,), 2, dtype=torch.int32, device=DEV)
+    gc.ag_push_shards(src, x["shards"], flags, ew, R=R, rank=rank)
     x["A"].copy_(new_shards[rank].to(DEV))
-    flags.fill_(2)
     out2, st2 = run_ag(x, R, rank, epoch=2, flags=flags)
     torch.cuda.synchronize()
     assert int(st2.item()) == 0
