@@ -267,11 +267,11 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
     `warm` launches of each (a fixed warm-up, past the power-limit transient
     of about 60 launches), then `blocks` timed blocks of `per_block` launches
     alternating in the order F U U F F U U F ... (each leg equally often
-    first).  Each block is timed with HIP events on the launch stream; the
-    shader clock is read from sysfs while each block runs.  Reports the
-    median block of each leg, then times the unfused parts alone.  (The
-    clock is read half-way through each block, by the warm-up's time per
-    launch.)"""
+    first).  Each block is timed with HIP events on the launch stream and
+    nothing else runs on the host meanwhile.  Reports the median block of
+    each leg, then reads the shader clock from sysfs during one more
+    (untimed) block of each leg, and times the unfused parts alone.  (A sysfs
+    clock read inside a timed block slowed that block by up to 15 %.)"""
     import torch
     parts = unfused_parts(w, x)
     legs = {"fused": fused_step, "unfused": parts["step"]}
@@ -286,7 +286,6 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
         torch.cuda.synchronize()
         est[name] = e0.elapsed_time(e1) / warm * 1e-3      # seconds per launch
     times = {"fused": [], "unfused": []}
-    clocks = {"fused": [], "unfused": []}
     for b in range(blocks):
         name = ("fused", "unfused", "unfused", "fused")[b % 4]
         f = legs[name]
@@ -295,12 +294,16 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
         for _ in range(per_block):
             f()
         e1.record(st)
-        # Read the clock while the block runs, half-way through (the read
-        # itself takes milliseconds; the events are already enqueued).
-        time.sleep(0.5 * per_block * est[name])
-        clocks[name] += read_sclk()
         torch.cuda.synchronize()
         times[name].append(e0.elapsed_time(e1) / per_block * 1e3)
+    clocks = {"fused": [], "unfused": []}
+    for name, f in legs.items():
+        n = max(per_block, int(0.02 / max(est[name], 1e-6)))   # at least 20 ms of work
+        for _ in range(n):
+            f()
+        time.sleep(0.5 * n * est[name])
+        clocks[name] += read_sclk()
+        torch.cuda.synchronize()
 
     def alone(f, n=20):
         if f is None:
@@ -323,7 +326,7 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
             "gather_us": alone(parts["gather"]), "what": parts["what"],
             "method": f"one window: {warm} warm-up launches of each leg, then {blocks} blocks of "
                       f"{per_block} launches alternating F U U F ...; median block per leg; sclk "
-                      "read from sysfs during each block"}
+                      "read from sysfs during one more, untimed block of each leg"}
 
 
 def ag_arrival(w, x, resident_us: float, iters: int = 10, warmup: int = 3) -> dict:
