@@ -269,9 +269,10 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
     alternating in the order F U U F F U U F ... (each leg equally often
     first).  Each block is timed with HIP events on the launch stream and
     nothing else runs on the host meanwhile.  Reports the median block of
-    each leg, then reads the shader clock from sysfs during one more
-    (untimed) block of each leg, and times the unfused parts alone.  (A sysfs
-    clock read inside a timed block slowed that block by up to 15 %.)"""
+    each leg, times the unfused parts alone (30 warm-up launches, then 40),
+    and reads the shader clock from sysfs during one more, untimed block of
+    each leg.  (A sysfs clock read inside a timed block slowed that block by
+    up to 15 %.)"""
     import torch
     parts = unfused_parts(w, x)
     legs = {"fused": fused_step, "unfused": parts["step"]}
@@ -296,19 +297,11 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
         e1.record(st)
         torch.cuda.synchronize()
         times[name].append(e0.elapsed_time(e1) / per_block * 1e3)
-    clocks = {"fused": [], "unfused": []}
-    for name, f in legs.items():
-        n = max(per_block, int(0.02 / max(est[name], 1e-6)))   # at least 20 ms of work
-        for _ in range(n):
-            f()
-        time.sleep(0.5 * n * est[name])
-        clocks[name] += read_sclk()
-        torch.cuda.synchronize()
 
-    def alone(f, n=20):
+    def alone(f, n=40, warm_n=30):
         if f is None:
             return 0.0
-        for _ in range(5):
+        for _ in range(warm_n):
             f()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(st)
@@ -318,12 +311,24 @@ def compare_fused_unfused(w, x, fused_step, blocks: int = 12, per_block: int = 2
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
 
+    # The unfused parts alone, right after the blocks (same window).
+    part_us = {k: alone(parts[k]) for k in ("gemm", "reduce", "gather")}
+    clocks = {"fused": [], "unfused": []}
+    for name, f in legs.items():
+        # At least 40 ms of work is queued; the clock is read as soon as it is
+        # (for short launches the host only just keeps ahead of the GPU).
+        n = max(per_block, int(0.04 / max(est[name], 1e-6)))
+        for _ in range(n):
+            f()
+        clocks[name] += read_sclk()
+        torch.cuda.synchronize()
+
     fu, uu = _median(times["fused"]), _median(times["unfused"])
     return {"fused_us": fu, "us_per_step": uu, "fused_speedup": uu / fu,
             "fused_blocks_us": times["fused"], "unfused_blocks_us": times["unfused"],
             "sclk_mhz_fused": _median(clocks["fused"]), "sclk_mhz_unfused": _median(clocks["unfused"]),
-            "gemm_us": alone(parts["gemm"]), "reduce_us": alone(parts["reduce"]),
-            "gather_us": alone(parts["gather"]), "what": parts["what"],
+            "gemm_us": part_us["gemm"], "reduce_us": part_us["reduce"],
+            "gather_us": part_us["gather"], "what": parts["what"],
             "method": f"one window: {warm} warm-up launches of each leg, then {blocks} blocks of "
                       f"{per_block} launches alternating F U U F ...; median block per leg; sclk "
                       "read from sysfs during one more, untimed block of each leg"}
