@@ -524,7 +524,7 @@ def main(argv=None) -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the peer ranks are emulated by buffers in this GPU's memory); "
               "run it with --gpus 1.", file=sys.stderr)
         return 2
