@@ -227,12 +227,6 @@ __device__ __forceinline__ void dma16_sys(u32x4_t r, uint32_t lds, uint32_t voff
                  : "memory");
 }
 
-// 8-byte buffer store.
-__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v)
-{
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
-}
-
 // fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ u32x2_t pack_bf16x4(f32x4_t v)
 {
@@ -241,6 +235,28 @@ __device__ __forceinline__ u32x2_t pack_bf16x4(f32x4_t v)
 }
 
 // Four bf16 (raw bits in two dwords) -> fp32, exactly.
+// Two neighbouring accumulator blocks of a row block (columns 16j .. 16j+31,
+// j even), packed to bf16 and regrouped so that every lane holds 8
+// consecutive columns of its row: lane (fi, fg) holds columns
+// 4fg .. 4fg+3 of each block, and the lanes of 16-lane rows 2k and 2k+1
+// (fg = 2k, 2k+1) trade halves with v_permlane16_swap (odd rows of its first
+// operand with even rows of its second), after which lane (fi, fg) holds
+// columns 8 (fg / 2) + 16 (fg % 2) .. +7 of the pair: block j's for even fg,
+// block j+1's for odd fg.  One 16-byte store per lane then writes 16 rows x
+// 64 bytes.  All 64 lanes must be active.
+__device__ __forceinline__ u32x4_t pack_pair(f32x4_t x, f32x4_t y)
+{
+    const u32x2_t px = pack_bf16x4(x), py = pack_bf16x4(y);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(px[0], py[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(px[1], py[1], false, false);
+    return (u32x4_t){s0[0], s1[0], s0[1], s1[1]};
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t unpack_bf16x4(u32x2_t w)
 {
     f32x4_t r;
@@ -772,7 +788,6 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         const int ln = opaque_v(lane);
         const int fi2 = ln & 15, fg2 = ln >> 4;
         const int pm_base2 = m0 + wm * WMt + fi2;
-        const int pn_base2 = n0 + wn * WN + 4 * fg2;
 
         // ---- split tile: exchange partials, finish the tile in shares ----
         // Each wave's 4*FMt accumulator blocks form NSEG = 2*FMt segments,
@@ -1025,10 +1040,13 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
             wait_vmcnt<0>();          // the two half-groups past the end
         }
 
-        // ---- epilogue: bf16 stores, 8 bytes per lane per block ----
+        // ---- epilogue: bf16 stores, 16 bytes per lane per pair of blocks ----
         // (of the owned segments only: in a split tile, the other units
-        // store the rest)
+        // store the rest; a segment is a pair of blocks, so a pair is owned
+        // or not as a whole)
         auto own = [&](int i, int j) { return ((smask >> (2 * i + (j >> 1))) & 1u) != 0; };
+        // first column of the lane's 8 in a pair of blocks (see pack_pair)
+        const int pn16 = n0 + wn * WN + 8 * (fg2 >> 1) + 16 * (fg2 & 1);
         if (MODE == MODE_RS) {
             // Two-shot AR: out is [M][N] (slice rows at their own index, rows
             // past M not stored) and the slice rows also go to every peer
@@ -1042,32 +1060,34 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
                 const int m = pm_base2 + 16 * i;
                 const bool in_slice = m >= s0 && m < s0 + p.P;
                 const bool to_ws = !in_slice && m < p.M;
-                const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn_base2 * 2u;
+                const uint32_t rbase = (uint32_t)(in_slice ? m - s0 : m) * N2 + (uint32_t)pn16 * 2u;
                 // The 16 rows of the block (uniform): all in the slice, all
                 // outside it, or straddling its edge (both stores, masked).
                 const int blk = m0 + wm * WMt + 16 * i;
                 const bool any_out = blk < s0 || blk + 16 > s0 + p.P;
                 const bool any_in = blk + 16 > s0 && blk < s0 + p.P;
                 const bool slice_st = in_slice && (!two || m < p.M);
-                const uint32_t obase = two ? (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u : rbase;
+                const uint32_t obase = two ? (uint32_t)m * N2 + (uint32_t)pn16 * 2u : rbase;
+                u32x4_t pk[FN / 2];
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const bool ok = pn_base2 + 16 * j < p.N && own(i, j);
-                    const u32x2_t v = pack_bf16x4(acc[i][j]);
+                for (int h = 0; h < FN / 2; ++h)
+                    pk[h] = pack_pair(acc[i][2 * h], acc[i][2 * h + 1]);
+#pragma unroll
+                for (int h = 0; h < FN / 2; ++h) {
+                    const bool ok = pn16 + 32 * h < p.N && own(i, 2 * h);
                     if (any_in)
-                        store8(ro, (ok && slice_st) ? obase + 32u * j : OOB, v);
+                        store16(ro, (ok && slice_st) ? obase + 64u * h : OOB, pk[h]);
                     if (any_out)
-                        store8(rw, (ok && to_ws) ? rbase + 32u * j : OOB, v);
+                        store16(rw, (ok && to_ws) ? rbase + 64u * h : OOB, pk[h]);
                 }
                 if (two && any_in) {
                     for (int q = 0; q < p.npeers; ++q) {
                         const __amdgpu_buffer_rsrc_t rq =
                             make_rsrc(p.peer_out + (size_t)q * p.M * p.N, (uint32_t)p.M * N2);
 #pragma unroll
-                        for (int j = 0; j < FN; ++j) {
-                            const bool ok = pn_base2 + 16 * j < p.N && own(i, j);
-                            store8(rq, (ok && slice_st) ? obase + 32u * j : OOB,
-                                   pack_bf16x4(acc[i][j]));
+                        for (int h = 0; h < FN / 2; ++h) {
+                            const bool ok = pn16 + 32 * h < p.N && own(i, 2 * h);
+                            store16(rq, (ok && slice_st) ? obase + 64u * h : OOB, pk[h]);
                         }
                     }
                 }
@@ -1078,11 +1098,11 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
 #pragma unroll
             for (int i = 0; i < FMt; ++i) {
                 const int m = pm_base2 + 16 * i;
-                const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn_base2 * 2u;
+                const uint32_t rbase = (uint32_t)m * N2 + (uint32_t)pn16 * 2u;
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const bool ok = m < p.M && pn_base2 + 16 * j < p.N && own(i, j);
-                    store8(ro, ok ? rbase + 32u * j : OOB, pack_bf16x4(acc[i][j]));
+                for (int h = 0; h < FN / 2; ++h) {
+                    const bool ok = m < p.M && pn16 + 32 * h < p.N && own(i, 2 * h);
+                    store16(ro, ok ? rbase + 64u * h : OOB, pack_pair(acc[i][2 * h], acc[i][2 * h + 1]));
                 }
             }
         }
