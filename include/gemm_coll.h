@@ -40,6 +40,8 @@
  *   that transpose), outputs [rows][N].
  * - All data pointers are device pointers on the current HIP device, 16-byte
  *   aligned; N and K must be multiples of 8 (rows are whole 16-byte vectors).
+ *   With K = 0 the operands that hold no element (A, B, AG's shards) may be
+ *   NULL.
  * - R, the tensor-parallel size, must satisfy 1 < R <= 16 and 128 % R == 0,
  *   i.e. R in {2, 4, 8, 16} (the validation chain of maybe_init_gemm_rs_ar,
  *   "[Kimi-K3] Extend GEMM-RS to GEMM-AR", 关键源码片段); 0 <= rank < R.

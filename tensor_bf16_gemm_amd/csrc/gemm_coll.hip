@@ -625,7 +625,8 @@ int ag_gemm(const gc_bf16 *A, const gc_bf16 *B, int64_t Ms, int64_t N, int64_t K
     int err = check_common(A, B, Ms, N, K, R, rank, peers, out);
     if (err || Ms == 0 || N == 0)
         return err;
-    if (!peers->shards || !aligned16(peers->shards) || !peers->flags ||
+    // (with K = 0 the shards hold no element and are never read)
+    if ((K > 0 && (!peers->shards || !aligned16(peers->shards))) || !peers->flags ||
         ((uintptr_t)peers->flags & 3u) || !peers->status || ((uintptr_t)peers->status & 3u))
         return GC_EINVAL;
     if (!fits(Ms, K) || !fits(K, N) || !fits(Ms * R, N))

@@ -4,6 +4,8 @@ Floating-point results must satisfy |gpu - ref| <= 1e-2*|ref| + 1e-2 element
 by element; row selection, slicing and indexing are checked bit-exactly with
 integer-valued inputs and row-ID encodings.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -344,6 +346,35 @@ def test_ag_sixteen_ranks_integer_all_ranks(orc, Ms, N, K, R):
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         assert_bits_equal(npb(out), ref, f"AG R=16 rank {rank}")
+
+
+@pytest.mark.parametrize("shards_null", [False, True])
+def test_ag_k0_gives_zeros(shards_null):
+    """AG-GEMM with K = 0: the output is all zeros, with the shards empty or
+    passed as a NULL pointer (they hold no element); the flags are still
+    waited on.  (A K = 0 call used to be refused when the empty shards
+    tensor had no storage.)"""
+    Ms, N, R, rank = 64, 56, 16, 13
+    shards = torch.empty((R, Ms, 0), dtype=torch.bfloat16, device=DEV)
+    A = torch.empty((Ms, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, N), dtype=torch.bfloat16, device=DEV)
+    flags = torch.ones(R, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.full((R * Ms, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    if shards_null:
+        peers = gc.GcPeers()
+        peers.shards = None
+        peers.flags = flags.data_ptr()
+        peers.status = status.data_ptr()
+        peers.epoch = 1
+        rc = gc.lib().ag_gemm(A.data_ptr(), B.data_ptr(), Ms, N, 0, R, rank, ctypes.byref(peers),
+                              out.data_ptr(), None)
+        assert rc == gc.GC_OK, gc.strerror(rc)
+    else:
+        gc.ag_gemm(A, B, shards, flags, status, out, R=R, rank=rank, epoch=1)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert bool((out.float() == 0).all()), "K = 0 must give zeros on every row"
 
 
 def test_ag_two_shards_withheld():
