@@ -597,8 +597,6 @@ __global__ __launch_bounds__(NT, 2) void gc_kernel(Args p)
         // so rows outside [row_lo, row_hi) read as zero (rows below wrap past
         // 2^31); chunks past N are masked per lane on edge tiles.  Items
         // outside [wlo, whi) load nothing (an empty buffer).
-        const int pm_base = m0 + wm * WMt + fi;
-        const int pn_base = n0 + wn * WN + 4 * fg;
         const int row_lo = MODE == MODE_RS ? p.lo : 0;
         const int row_hi = MODE == MODE_RS ? p.hi : p.M;
         int W = 0;
