@@ -6,7 +6,6 @@ polls the flags.  The output must equal the oracle's bit for bit on integer
 inputs, with no time-out, in two rounds on the same receive buffer (new
 shard contents and a new epoch: a stale cached copy of the first round's
 shards would show)."""
-import numpy as np
 import pytest
 import torch
 

@@ -49,7 +49,6 @@ def test_pins_catch_planted_mistake(plant, tmp_path):
 
 def test_oracle_thread_count_independent(orc):
     """Rows are split whole over threads: one thread and many give the same bits."""
-    import numpy as np
     import subprocess
     import sys
     code = (

@@ -5,7 +5,6 @@ all three modes -- ragged M, N and K, a last row tile that is mostly empty,
 K shorter than the peer items (their drain after the K loop), and every RS
 rank.  Also: the automatic choice at M=4096 against forced 256-row tiles on
 float inputs, and the argument check."""
-import ctypes
 
 import numpy as np
 import pytest
